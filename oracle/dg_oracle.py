@@ -1,0 +1,288 @@
+"""Plain CPU oracle for the fine-grained-scaled FP8 NT GEMM and its M-grouped
+variants.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this module. The GPU library never calls it, and
+it shares no code with the GPU library: it reads raw bytes (uint8 FP8 codes,
+float32 scales, int32 layouts, uint16 BF16 bit patterns) as numpy arrays.
+
+What it computes is the plain definition of the operation, in float64:
+
+    dec(q)     value of the OCP E4M3 byte q
+    Ahat[m,k]  = dec(A[m,k]) * sfa[k // 128][m]          (LHS: one scale per 1x128)
+    Bhat[n,k]  = dec(B[n,k]) * sfb[n // 128][k // 128]   (RHS: one scale per 128x128)
+    D[m,n]     = bf16_rne( sum_k Ahat[m,k] * Bhat[n,k] )
+
+Sources on the pages:
+  * "DeepGEMM for PPU" README, "Interfaces > Notices": kernels are NT only
+    (LHS row-major, RHS stored transposed, i.e. [N, K]); the LHS scaling
+    factors are stored transposed (M-major) with an aligned leading dimension.
+  * same page, "Normal dense GEMMs (non-grouped)": the dense FP8 x FP8 -> BF16
+    NT GEMM.
+  * same page, "Grouped GEMMs (contiguous layout)": only M is grouped, N and K
+    are shared by every group; expert segments are concatenated along M and
+    each is aligned to the M block size.
+  * same page, "Grouped GEMMs (masked layout)": a per-group count of valid
+    rows; only the valid part of each group is computed.
+  * "DeepGEMM Compatibility Wrapper (deep-gemm)" page, "0.2.7 Compatibility
+    Additions" and "Contiguous Grouped GEMM Alignment": scale recipe
+    (1, 128, 128) and the 128-row segment alignment.
+
+The 128-K block structure of the scales does not change the definition: the
+per-block sums scaled and added are algebraically the plain sum over the
+dequantised operands, which is what is written here.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+  * FP8 flavour: OCP E4M3 (bias 7, max 448, codes 0x7F/0xFF are NaN, no inf).
+  * BF16 rounding: round to nearest, ties to even, applied once to the exact
+    float64 sum (no intermediate rounding to float32).
+  * contiguous layout: row m belongs to group L[m] when 0 <= L[m] < G; any
+    other id (-1 marks padding) leaves row m of D untouched.
+  * masked layout: masked_m[g] is clamped to [0, max_m]; rows at or beyond it
+    are left untouched.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "BLOCK_K",
+    "e4m3_value",
+    "e4m3_decode_table",
+    "bf16_round",
+    "bf16_bits",
+    "bf16_bits_to_f64",
+    "dequant_lhs",
+    "dequant_rhs",
+    "gemm_nt_f64",
+    "dense_f64_at",
+    "fp8_gemm_nt",
+    "m_grouped_fp8_gemm_nt_contiguous",
+    "m_grouped_fp8_gemm_nt_masked",
+    "contiguous_f64_at",
+    "masked_f64_at",
+]
+
+# Scale granularity along K for both operands: recipe (1, 128, 128).
+BLOCK_K = 128
+
+
+# ---------------------------------------------------------------------------
+# Number formats
+# ---------------------------------------------------------------------------
+
+def e4m3_value(code: int) -> float:
+    """Value of one OCP E4M3 byte (OCP 8-bit floating point specification).
+
+    Layout: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0.
+    Exponent field 0 encodes subnormals (f/8 * 2^-6); exponent field 15 with
+    mantissa 7 is NaN; there is no infinity, so 0x7E (= 448) is the largest
+    finite value.
+    """
+    sign = -1.0 if (code >> 7) & 1 else 1.0
+    exp_field = (code >> 3) & 0xF
+    man_field = code & 0x7
+    if exp_field == 0xF and man_field == 0x7:
+        return float("nan")
+    if exp_field == 0:
+        return sign * (man_field / 8.0) * 2.0 ** -6
+    return sign * (1.0 + man_field / 8.0) * 2.0 ** (exp_field - 7)
+
+
+def e4m3_decode_table() -> np.ndarray:
+    """All 256 E4M3 values as float64, indexed by the byte."""
+    return np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def bf16_round(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 has 8 significant bits and float32's exponent range: a finite
+    value with binary exponent E (|x| in [2^E, 2^(E+1))) is a multiple of
+    2^(E-7); below 2^-126 the spacing stays 2^-133 (subnormals). A result of
+    magnitude 2^128 or more is out of range and becomes infinity. The result
+    is returned as float64 holding the exact bfloat16 value.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, dtype=np.float64, copy=True)
+    finite = np.isfinite(x)
+    ax = np.abs(x[finite])
+    _, e = np.frexp(ax)                      # ax = mant * 2^e, mant in [0.5, 1)
+    exponent = np.maximum(e - 1, -126)       # E with the subnormal floor
+    quantum = np.ldexp(1.0, exponent - 7)
+    y = np.rint(ax / quantum) * quantum      # rint rounds half to even
+    y = np.where(y >= 2.0 ** 128, np.inf, y)
+    out[finite] = np.copysign(y, x[finite])
+    return out
+
+
+def bf16_bits(x) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of float64 values, rounded to nearest even.
+
+    The bfloat16 encoding is the upper half of the float32 encoding of the same
+    value; every bfloat16 value is exact in float32. NaN maps to 0x7FC0.
+    """
+    y = bf16_round(x).astype(np.float32)
+    bits = (y.view(np.uint32) >> 16).astype(np.uint16)
+    bits[np.isnan(y)] = 0x7FC0
+    return bits
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Values of bfloat16 bit patterns, as float64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Dequantisation
+# ---------------------------------------------------------------------------
+
+def dequant_lhs(a_codes: np.ndarray, sfa: np.ndarray) -> np.ndarray:
+    """Ahat[m,k] = dec(A[m,k]) * sfa[k // 128][m].
+
+    a_codes: uint8 [M, K] (row-major, K contiguous).
+    sfa:     float32 [K/128, ld] with ld >= M: the LHS scales stored
+             transposed (M-major) with an aligned leading dimension.
+    """
+    a_codes = np.asarray(a_codes, dtype=np.uint8)
+    m_rows, k = a_codes.shape
+    assert k % BLOCK_K == 0
+    assert sfa.shape[0] == k // BLOCK_K and sfa.shape[1] >= m_rows
+    values = e4m3_decode_table()[a_codes]                       # [M, K]
+    scale = np.asarray(sfa, dtype=np.float64)[:, :m_rows].T     # [M, K/128]
+    return values * np.repeat(scale, BLOCK_K, axis=1)
+
+
+def dequant_rhs(b_codes: np.ndarray, sfb: np.ndarray) -> np.ndarray:
+    """Bhat[n,k] = dec(B[n,k]) * sfb[n // 128][k // 128].
+
+    b_codes: uint8 [N, K] (the transposed RHS of the NT product).
+    sfb:     float32 [ceil(N/128), K/128].
+    """
+    b_codes = np.asarray(b_codes, dtype=np.uint8)
+    n, k = b_codes.shape
+    assert k % BLOCK_K == 0
+    assert sfb.shape == ((n + BLOCK_K - 1) // BLOCK_K, k // BLOCK_K)
+    values = e4m3_decode_table()[b_codes]                       # [N, K]
+    scale = np.asarray(sfb, dtype=np.float64)
+    scale = np.repeat(np.repeat(scale, BLOCK_K, axis=0)[:n], BLOCK_K, axis=1)
+    return values * scale
+
+
+def gemm_nt_f64(a_codes, sfa, b_codes, sfb) -> np.ndarray:
+    """Unrounded float64 result sum_k Ahat[m,k] * Bhat[n,k], shape [M, N]."""
+    ahat = dequant_lhs(a_codes, sfa)
+    bhat = dequant_rhs(b_codes, sfb)
+    return ahat @ bhat.T
+
+
+# ---------------------------------------------------------------------------
+# The three operations (output: uint16 BF16 bit patterns)
+# ---------------------------------------------------------------------------
+
+def fp8_gemm_nt(a_codes, sfa, b_codes, sfb, d_init=None) -> np.ndarray:
+    """Dense FP8 NT GEMM: D[m,n] = bf16(sum_k Ahat[m,k] Bhat[n,k]) for all rows.
+
+    d_init is accepted for a uniform interface; every element is written.
+    """
+    d = bf16_bits(gemm_nt_f64(a_codes, sfa, b_codes, sfb))
+    if d_init is not None:
+        assert d_init.shape == d.shape
+    return d
+
+
+def m_grouped_fp8_gemm_nt_contiguous(a_codes, sfa, b_codes, sfb, layout, d_init) -> np.ndarray:
+    """M-grouped GEMM, contiguous layout.
+
+    a_codes [M, K], sfa [K/128, ld], b_codes [G, N, K], sfb [G, N/128, K/128],
+    layout int32 [M] (group of each row; -1 or any id outside [0, G) marks a
+    row that is not computed), d_init uint16 [M, N] (prior contents of D).
+    Row m of D becomes bf16(Ahat[m] . Bhat_{L[m]}^T) when 0 <= L[m] < G and is
+    copied from d_init otherwise.
+    """
+    layout = np.asarray(layout, dtype=np.int64)
+    num_groups = b_codes.shape[0]
+    d = np.array(d_init, dtype=np.uint16, copy=True)
+    for g in range(num_groups):
+        rows = np.nonzero(layout == g)[0]
+        if rows.size == 0:
+            continue
+        ahat = dequant_lhs(a_codes[rows], sfa[:, rows])
+        bhat = dequant_rhs(b_codes[g], sfb[g])
+        d[rows] = bf16_bits(ahat @ bhat.T)
+    return d
+
+
+def m_grouped_fp8_gemm_nt_masked(a_codes, sfa, b_codes, sfb, masked_m, d_init) -> np.ndarray:
+    """M-grouped GEMM, masked layout.
+
+    a_codes [G, max_m, K], sfa [G, K/128, ld], b_codes [G, N, K],
+    sfb [G, N/128, K/128], masked_m int32 [G], d_init uint16 [G, max_m, N].
+    For each group g, rows m < clamp(masked_m[g], 0, max_m) of D[g] become
+    bf16(Ahat_g[m] . Bhat_g^T); all other rows keep d_init's contents.
+    """
+    num_groups, max_m, _ = a_codes.shape
+    d = np.array(d_init, dtype=np.uint16, copy=True)
+    for g in range(num_groups):
+        valid = int(min(max(int(masked_m[g]), 0), max_m))
+        if valid == 0:
+            continue
+        ahat = dequant_lhs(a_codes[g, :valid], sfa[g])
+        bhat = dequant_rhs(b_codes[g], sfb[g])
+        d[g, :valid] = bf16_bits(ahat @ bhat.T)
+    return d
+
+
+# ---------------------------------------------------------------------------
+# Sampled evaluation for full-size checks: a subset of rows and columns.
+# ---------------------------------------------------------------------------
+
+def _rows_cols_f64(a_codes, sfa, b_codes, sfb, rows, cols) -> np.ndarray:
+    """sum_k Ahat[r,k] Bhat[c,k] for r in rows, c in cols (one group)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    k = a_codes.shape[1]
+    table = e4m3_decode_table()
+    a_val = table[np.asarray(a_codes[rows], dtype=np.uint8)]
+    a_scale = np.asarray(sfa, dtype=np.float64)[:, rows].T
+    ahat = a_val * np.repeat(a_scale, BLOCK_K, axis=1)
+    b_val = table[np.asarray(b_codes[cols], dtype=np.uint8)]
+    b_scale = np.asarray(sfb, dtype=np.float64)[cols // BLOCK_K]
+    bhat = b_val * np.repeat(b_scale, BLOCK_K, axis=1)
+    assert ahat.shape[1] == k and bhat.shape[1] == k
+    return ahat @ bhat.T
+
+
+def dense_f64_at(a_codes, sfa, b_codes, sfb, rows, cols) -> np.ndarray:
+    """Unrounded dense result at rows x cols."""
+    return _rows_cols_f64(a_codes, sfa, b_codes, sfb, rows, cols)
+
+
+def contiguous_f64_at(a_codes, sfa, b_codes, sfb, layout, rows, cols) -> np.ndarray:
+    """Unrounded contiguous-layout result at rows x cols; NaN where a row is
+    not computed (its group id is outside [0, G))."""
+    layout = np.asarray(layout, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.full((rows.size, len(cols)), np.nan)
+    for g in range(b_codes.shape[0]):
+        sel = np.nonzero(layout[rows] == g)[0]
+        if sel.size:
+            out[sel] = _rows_cols_f64(a_codes, sfa, b_codes[g], sfb[g], rows[sel], cols)
+    return out
+
+
+def masked_f64_at(a_codes, sfa, b_codes, sfb, masked_m, group, rows, cols) -> np.ndarray:
+    """Unrounded masked-layout result of one group at rows x cols; NaN for
+    rows at or beyond the group's clamped valid count."""
+    max_m = a_codes.shape[1]
+    valid = int(min(max(int(masked_m[group]), 0), max_m))
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.full((rows.size, len(cols)), np.nan)
+    sel = np.nonzero(rows < valid)[0]
+    if sel.size:
+        out[sel] = _rows_cols_f64(a_codes[group], sfa[group], b_codes[group], sfb[group], rows[sel], cols)
+    return out

@@ -1,0 +1,461 @@
+"""Pins for the oracle's GEMM, independent of the oracle itself.
+
+Each pin checks the oracle against something other than its own code:
+  * exact rational arithmetic (fractions.Fraction) on tiny inputs, with an
+    exact round-to-nearest-even to BF16 written on rationals;
+  * integer-exact inputs (codes in {-2..2}, power-of-two scales that differ
+    per K block, per row and per N block) against a per-block integer closed
+    form;
+  * all scales 1: torch float64 matmul of the decoded operands;
+  * constant operands: a closed form in the scales alone;
+  * invariants: grouped == per-group dense, permuting segments permutes rows,
+    masked and padding rows untouched, NaN-poisoned padding does not leak.
+
+test_planted_mistakes_are_caught plants plausible mistakes in a private copy
+of the oracle (wrong scale index, transposed RHS scales, wrong FP8 flavour,
+truncating or double rounding, dropped K block, missing sign, padding rows
+written, off-by-one masks) and checks that at least one pin fails for each.
+"""
+
+import importlib.util
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dg_oracle as O
+
+ORACLE_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "dg_oracle.py")
+
+CODE_OF = {0: 0x00, 1: 0x38, 2: 0x40, -1: 0xB8, -2: 0xC0}   # E4M3 codes of small integers
+
+
+# ---------------------------------------------------------------------------
+# Independent helpers
+# ---------------------------------------------------------------------------
+
+def _decode_torch(codes: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _bf16_rne_exact(v: Fraction) -> int:
+    """BF16 bits of a rational, rounded to nearest even, in exact arithmetic."""
+    if v == 0:
+        return 0
+    neg = v < 0
+    a = -v if neg else v
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    quantum = Fraction(2) ** (e - 7)
+    t = a / quantum
+    n = t.numerator // t.denominator
+    rem = t - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    val = n * quantum
+    if val >= Fraction(2) ** 128:
+        bits = 0x7F80
+    else:
+        bits = int(np.array([float(val)], dtype=np.float32).view(np.uint32)[0] >> 16)
+    return bits | (0x8000 if neg else 0)
+
+
+def _random_inputs(rng, m, n, k, groups=None):
+    """Random codes (finite, not NaN) and random positive float32 scales."""
+    def codes(shape):
+        c = rng.integers(0, 256, size=shape).astype(np.uint8)
+        c[(c & 0x7F) == 0x7F] = 0x3C  # replace NaN codes
+        return c
+
+    def scales(shape):
+        return (rng.uniform(0.25, 4.0, size=shape)).astype(np.float32)
+
+    a = codes((m, k))
+    sfa = scales((k // 128, (m + 3) // 4 * 4))
+    if groups is None:
+        return a, sfa, codes((n, k)), scales((n // 128, k // 128))
+    return a, sfa, codes((groups, n, k)), scales((groups, n // 128, k // 128))
+
+
+def _exact_gemm(a, sfa, b, sfb):
+    """Exact rational sum_k dec(a) sa * dec(b) sb, as a list of lists of Fractions."""
+    m, k = a.shape
+    n = b.shape[0]
+    av = _decode_torch(a)
+    bv = _decode_torch(b)
+    fa = [[Fraction(float(av[i, kk])) * Fraction(float(sfa[kk // 128, i])) for kk in range(k)] for i in range(m)]
+    fb = [[Fraction(float(bv[j, kk])) * Fraction(float(sfb[j // 128, kk // 128])) for kk in range(k)] for j in range(n)]
+    return [[sum(x * y for x, y in zip(fa[i], fb[j])) for j in range(n)] for i in range(m)], fa, fb
+
+
+def _check_against_exact(oracle_f64, oracle_bits, exact, fa, fb):
+    m, n = len(exact), len(exact[0])
+    k = len(fa[0])
+    checked = 0
+    for i in range(m):
+        for j in range(n):
+            ex = exact[i][j]
+            abs_terms = sum(abs(x * y) for x, y in zip(fa[i], fb[j]))
+            bound = float(abs_terms) * 2 * k * 2.0 ** -53 + 1e-300
+            assert abs(oracle_f64[i, j] - float(ex)) <= bound, (i, j)
+            # skip elements so close to a BF16 midpoint that fp64 rounding may flip it
+            lo = _bf16_rne_exact(ex - Fraction(bound))
+            hi = _bf16_rne_exact(ex + Fraction(bound))
+            if lo != hi:
+                continue
+            assert int(oracle_bits[i, j]) == _bf16_rne_exact(ex), (i, j)
+            checked += 1
+    assert checked >= 0.95 * m * n
+
+
+# ---------------------------------------------------------------------------
+# Pins, written as functions of an oracle module so that they can also run
+# against planted-mistake copies.
+# ---------------------------------------------------------------------------
+
+def pin_exact_dense(orc):
+    rng = np.random.default_rng(7)
+    a, sfa, b, sfb = _random_inputs(rng, 3, 256, 256)
+    exact, fa, fb = _exact_gemm(a, sfa, b, sfb)
+    f64 = orc.gemm_nt_f64(a, sfa, b, sfb)
+    bits = orc.fp8_gemm_nt(a, sfa, b, sfb)
+    _check_against_exact(f64, bits, exact, fa, fb)
+
+
+def pin_exact_grouped(orc):
+    rng = np.random.default_rng(11)
+    a, sfa, b, sfb = _random_inputs(rng, 256, 128, 256, groups=2)
+    layout = np.full(256, -1, dtype=np.int32)
+    layout[0:2] = 0
+    layout[128:131] = 1
+    d0 = np.full((256, 128), 0xFFFF, dtype=np.uint16)
+    d = orc.m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, layout, d0)
+    for g, rows in ((0, [0, 1]), (1, [128, 129, 130])):
+        sub_a = a[rows]
+        sub_sfa = sfa[:, rows]
+        sub_sfa = np.pad(sub_sfa, ((0, 0), (0, (-len(rows)) % 4)))
+        exact, fa, fb = _exact_gemm(sub_a, sub_sfa, b[g], sfb[g])
+        for ii, r in enumerate(rows):
+            for j in range(128):
+                assert int(d[r, j]) == _bf16_rne_exact(exact[ii][j]) or abs(
+                    float(O.bf16_bits_to_f64(d[r, j])) - float(exact[ii][j])) <= 2.0 ** -7 * abs(float(exact[ii][j]))
+    untouched = np.ones(256, bool)
+    untouched[[0, 1, 128, 129, 130]] = False
+    assert np.all(d[untouched] == 0xFFFF)
+
+
+def _int_exact_case(rng, m, n, k):
+    vals_a = rng.integers(-2, 3, size=(m, k))
+    vals_b = rng.integers(-2, 3, size=(n, k))
+    a = np.vectorize(CODE_OF.get)(vals_a).astype(np.uint8)
+    b = np.vectorize(CODE_OF.get)(vals_b).astype(np.uint8)
+    ld = (m + 3) // 4 * 4
+    # exponents that differ with the K block and the row / N block
+    ea = (np.arange(k // 128)[:, None] * 3 + np.arange(ld)[None, :]) % 3 - 1        # in {-1, 0, 1}
+    eb = (np.arange(n // 128)[:, None] * 2 + np.arange(k // 128)[None, :] * 5) % 3 - 1
+    sfa = np.ldexp(1.0, ea).astype(np.float32)
+    sfb = np.ldexp(1.0, eb).astype(np.float32)
+    return vals_a, vals_b, a, sfa, b, sfb, ea, eb
+
+
+def pin_integer_closed_form(orc):
+    rng = np.random.default_rng(3)
+    m, n, k = 12, 256, 640
+    vals_a, vals_b, a, sfa, b, sfb, ea, eb = _int_exact_case(rng, m, n, k)
+    f64 = orc.gemm_nt_f64(a, sfa, b, sfb)
+    bits = orc.fp8_gemm_nt(a, sfa, b, sfb)
+    for i in range(m):
+        for j in range(n):
+            total = Fraction(0)
+            for kb in range(k // 128):
+                s = int(np.dot(vals_a[i, kb * 128:(kb + 1) * 128], vals_b[j, kb * 128:(kb + 1) * 128]))
+                total += s * Fraction(2) ** int(ea[kb, i] + eb[j // 128, kb])
+            assert f64[i, j] == float(total), (i, j, f64[i, j], total)
+            assert int(bits[i, j]) == _bf16_rne_exact(total), (i, j)
+
+
+def pin_unit_scales_matmul(orc):
+    rng = np.random.default_rng(5)
+    a, _, b, _ = _random_inputs(rng, 40, 256, 384)
+    sfa = np.ones((3, 40), np.float32)
+    sfb = np.ones((2, 3), np.float32)
+    ref = torch.from_numpy(_decode_torch(a)) @ torch.from_numpy(_decode_torch(b)).T
+    got = orc.gemm_nt_f64(a, sfa, b, sfb)
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def pin_constant_operands(orc):
+    # A all 1.5 (code 0x3C), B all -3 (code 0xC4): D[m,n] = 128 * 1.5 * -3 * sum_kb sa[kb][m] sb[n//128][kb]
+    m, n, k = 6, 384, 512
+    a = np.full((m, k), 0x3C, np.uint8)
+    b = np.full((n, k), 0xC4, np.uint8)
+    sfa = (np.arange(k // 128)[:, None] + 1.0 + 0.25 * np.arange(8)[None, :]).astype(np.float32)
+    sfb = (0.5 + np.arange(n // 128)[:, None] * 2.0 + np.arange(k // 128)[None, :] * 0.125).astype(np.float32)
+    got = orc.gemm_nt_f64(a, sfa, b, sfb)
+    for i in range(m):
+        for j in range(n):
+            expect = 128 * 1.5 * -3.0 * sum(float(sfa[kb, i]) * float(sfb[j // 128, kb]) for kb in range(k // 128))
+            assert math.isclose(got[i, j], expect, rel_tol=1e-13), (i, j)
+
+
+def pin_grouped_is_per_group_dense(orc):
+    rng = np.random.default_rng(9)
+    rows = [130, 0, 77, 256]
+    layout = np.concatenate([np.r_[np.full(r, g), np.full((-r) % 128, -1)] for g, r in enumerate(rows)]).astype(np.int32)
+    m = layout.size
+    a, sfa, b, sfb = _random_inputs(rng, m, 256, 256, groups=len(rows))
+    d0 = np.full((m, 256), 0xFFFF, np.uint16)
+    d = orc.m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, layout, d0)
+    for g in range(len(rows)):
+        idx = np.nonzero(layout == g)[0]
+        if idx.size == 0:
+            continue
+        sub_sfa = np.pad(sfa[:, idx], ((0, 0), (0, (-idx.size) % 4)))
+        dense = orc.fp8_gemm_nt(a[idx], sub_sfa, b[g], sfb[g])
+        assert np.array_equal(d[idx], dense)
+    assert np.all(d[layout < 0] == 0xFFFF)
+    # permuting whole segments permutes the output rows
+    segs, start = [], 0
+    for g, r in enumerate(rows):
+        p = r + (-r) % 128
+        segs.append(np.arange(start, start + p))
+        start += p
+    order = [3, 0, 2, 1]
+    perm = np.concatenate([segs[i] for i in order])
+    sfa_p = np.pad(sfa[:, perm], ((0, 0), (0, sfa.shape[1] - perm.size)))
+    d_p = orc.m_grouped_fp8_gemm_nt_contiguous(a[perm], sfa_p, b, sfb, layout[perm], d0)
+    assert np.array_equal(d_p, d[perm])
+
+
+def pin_masked_rows(orc):
+    rng = np.random.default_rng(13)
+    g_count, max_m, n, k = 4, 40, 128, 256
+    a, _, b, sfb = _random_inputs(rng, g_count * max_m, n, k, groups=g_count)
+    a = a.reshape(g_count, max_m, k).copy()
+    sfa = rng.uniform(0.5, 2, size=(g_count, k // 128, max_m)).astype(np.float32)
+    masked = np.array([0, 1, 40, 17], np.int32)
+    for g in range(g_count):
+        a[g, masked[g]:] = 0x7F   # NaN beyond the valid rows must not leak
+    d0 = np.full((g_count, max_m, n), 0xFFFF, np.uint16)
+    d = orc.m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, masked, d0)
+    for g in range(g_count):
+        v = masked[g]
+        assert np.all(d[g, v:] == 0xFFFF)
+        if v:
+            dense = orc.fp8_gemm_nt(a[g, :v], sfa[g], b[g], sfb[g])
+            assert np.array_equal(d[g, :v], dense)
+            assert not np.any(np.isnan(O.bf16_bits_to_f64(d[g, :v])))
+    # out-of-range counts are clamped
+    d2 = orc.m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, np.array([-5, 1, 99, 17], np.int32), d0)
+    assert np.array_equal(d2[1:3], d[1:3]) and np.all(d2[0] == 0xFFFF)
+
+
+def pin_contiguous_poisoned_padding(orc):
+    rng = np.random.default_rng(17)
+    rows = [5, 128, 1]
+    layout = np.concatenate([np.r_[np.full(r, g), np.full((-r) % 128, -1)] for g, r in enumerate(rows)]).astype(np.int32)
+    m = layout.size
+    a, sfa, b, sfb = _random_inputs(rng, m, 128, 256, groups=3)
+    a[layout < 0] = 0x7F
+    d = orc.m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, layout, np.full((m, 128), 0xFFFF, np.uint16))
+    assert np.all(d[layout < 0] == 0xFFFF)
+    assert not np.any(np.isnan(O.bf16_bits_to_f64(d[layout >= 0])))
+
+
+def pin_sampled_matches_full(orc):
+    rng = np.random.default_rng(19)
+    a, sfa, b, sfb = _random_inputs(rng, 64, 384, 384)
+    full = orc.gemm_nt_f64(a, sfa, b, sfb)
+    rows, cols = np.array([0, 5, 63]), np.array([1, 200, 383])
+    # same sums, possibly a different BLAS summation order: equal to fp64 rounding
+    np.testing.assert_allclose(orc.dense_f64_at(a, sfa, b, sfb, rows, cols), full[np.ix_(rows, cols)],
+                               rtol=1e-12, atol=1e-9)
+
+
+def pin_formats_golden(orc):
+    """The hand-derived E4M3 and BF16 tables in tests/golden."""
+    import test_oracle_formats as F
+    F.check_e4m3_golden(orc)
+    F.check_bf16_golden(orc)
+
+
+def pin_near_tie_gemm(orc):
+    """A product whose exact value is just above a BF16 tie: 1 + 2^-8 + 2^-34.
+
+    Row 0 of A is [1, 2^-4, 0...] in block 0 and [2^-9, 0...] in block 1;
+    row 0 of B is [1, 2^-4, 0...] in block 0 and [1, 0...] in block 1; the
+    second K block carries scales 2^-10 (A) and 2^-15 (B). A single rounding
+    gives 1 + 2^-7; rounding through float32 first gives 1.0.
+    """
+    k = 256
+    a = np.zeros((1, k), np.uint8)
+    b = np.zeros((128, k), np.uint8)
+    a[0, 0], a[0, 1], a[0, 128] = 0x38, 0x18, 0x01        # 1, 2^-4, 2^-9
+    b[0, 0], b[0, 1], b[0, 128] = 0x38, 0x18, 0x38        # 1, 2^-4, 1
+    sfa = np.array([[1.0, 0, 0, 0], [2.0 ** -10, 0, 0, 0]], np.float32)
+    sfb = np.array([[1.0, 2.0 ** -15]], np.float32)
+    f64 = orc.gemm_nt_f64(a, sfa, b, sfb)
+    assert f64[0, 0] == 1.0 + 2.0 ** -8 + 2.0 ** -34
+    assert int(orc.fp8_gemm_nt(a, sfa, b, sfb)[0, 0]) == 0x3F81
+
+
+PINS = [
+    pin_formats_golden,
+    pin_near_tie_gemm,
+    pin_exact_dense,
+    pin_exact_grouped,
+    pin_integer_closed_form,
+    pin_unit_scales_matmul,
+    pin_constant_operands,
+    pin_grouped_is_per_group_dense,
+    pin_masked_rows,
+    pin_contiguous_poisoned_padding,
+    pin_sampled_matches_full,
+]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin_holds(pin):
+    pin(O)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each must break at least one pin
+# ---------------------------------------------------------------------------
+
+def _fresh_oracle():
+    spec = importlib.util.spec_from_file_location("dg_oracle_mutant", ORACLE_PATH)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _mut_lhs_scale_first_row(mod):
+    orig = mod.dequant_lhs
+
+    def f(a_codes, sfa):
+        s = np.repeat(np.asarray(sfa)[:, :1], sfa.shape[1], axis=1)
+        return orig(a_codes, s)
+    mod.dequant_lhs = f
+
+
+def _mut_rhs_scale_transposed(mod):
+    def f(b_codes, sfb):
+        n, k = b_codes.shape
+        v = mod.e4m3_decode_table()[b_codes]
+        s = np.asarray(sfb, np.float64)
+        # reads sfb[kb][nb] instead of sfb[nb][kb] (wraps when the shape is not square)
+        idx_n = np.arange(n) // 128
+        idx_k = np.arange(k) // 128
+        flat = s.reshape(-1)
+        scale = flat[(idx_k[None, :] * s.shape[1] + idx_n[:, None]) % flat.size]
+        return v * scale
+    mod.dequant_rhs = f
+
+
+def _mut_fnuz(mod):
+    def table():
+        t = np.empty(256)
+        for c in range(256):
+            s = -1.0 if c >> 7 else 1.0
+            e, f = (c >> 3) & 15, c & 7
+            t[c] = s * ((f / 8) * 2.0 ** -7 if e == 0 else (1 + f / 8) * 2.0 ** (e - 8))
+        t[0x80] = np.nan
+        return t
+    mod.e4m3_decode_table = table
+
+
+def _mut_truncate(mod):
+    def bits(x):
+        y = np.asarray(x, np.float64).astype(np.float32)
+        return (y.view(np.uint32) >> 16).astype(np.uint16)
+    mod.bf16_bits = bits
+
+
+def _mut_double_round(mod):
+    orig = mod.bf16_bits
+
+    def bits(x):
+        return orig(np.asarray(x, np.float64).astype(np.float32).astype(np.float64))
+    mod.bf16_bits = bits
+
+
+def _mut_drop_last_kblock(mod):
+    orig = mod.dequant_lhs
+
+    def f(a_codes, sfa):
+        r = orig(a_codes, sfa)
+        r[:, -128:] = 0.0
+        return r
+    mod.dequant_lhs = f
+
+
+def _mut_no_sign(mod):
+    orig = mod.e4m3_decode_table
+
+    def table():
+        return np.abs(orig())
+    mod.e4m3_decode_table = table
+
+
+def _mut_padding_written(mod):
+    orig = mod.m_grouped_fp8_gemm_nt_contiguous
+
+    def f(a_codes, sfa, b_codes, sfb, layout, d_init):
+        lay = np.where(np.asarray(layout) < 0, 0, layout)
+        return orig(a_codes, sfa, b_codes, sfb, lay, d_init)
+    mod.m_grouped_fp8_gemm_nt_contiguous = f
+
+
+def _mut_masked_off_by_one(mod):
+    orig = mod.m_grouped_fp8_gemm_nt_masked
+
+    def f(a_codes, sfa, b_codes, sfb, masked_m, d_init):
+        return orig(a_codes, sfa, b_codes, sfb, np.asarray(masked_m) + 1, d_init)
+    mod.m_grouped_fp8_gemm_nt_masked = f
+
+
+def _mut_lhs_scale_by_k_only(mod):
+    # applies sfa[kb][kb] (diagonal) instead of sfa[kb][m]
+    def f(a_codes, sfa):
+        m, k = a_codes.shape
+        v = mod.e4m3_decode_table()[np.asarray(a_codes, np.uint8)]
+        kb = np.arange(k) // 128
+        s = np.asarray(sfa, np.float64)[kb, kb % sfa.shape[1]]
+        return v * s[None, :]
+    mod.dequant_lhs = f
+
+
+MUTANTS = [
+    _mut_lhs_scale_first_row,
+    _mut_rhs_scale_transposed,
+    _mut_fnuz,
+    _mut_truncate,
+    _mut_double_round,
+    _mut_drop_last_kblock,
+    _mut_no_sign,
+    _mut_padding_written,
+    _mut_masked_off_by_one,
+    _mut_lhs_scale_by_k_only,
+]
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=[m.__name__ for m in MUTANTS])
+def test_planted_mistakes_are_caught(mutant):
+    mod = _fresh_oracle()
+    mutant(mod)
+    failures = 0
+    for pin in PINS:
+        try:
+            pin(mod)
+        except (AssertionError, ValueError, IndexError):
+            failures += 1
+    assert failures >= 1, f"no pin caught {mutant.__name__}"
