@@ -1,0 +1,218 @@
+"""Benchmark of the FP8 NT GEMM (1x128 / 128x128 float32 scales, BF16 out).
+
+One step = one call of the GEMM on one batch of synthetic input already in
+HBM. The headline workload is the dense 4096x7168x2048 GEMM; the grouped
+contiguous, masked-decode and small dense workloads are measured after it
+and reported under "workloads". Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only INDEX]
+                    [--no-cpu-baseline] [--no-extra] [--copy-calibration]
+
+--only INDEX times a single workload (0..4), for profiling runs.
+--copy-calibration runs a plain 1 GiB device copy (for scaling HBM traffic
+counters) and exits.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOPS & % FP8 MFMA peak: dense, m-grouped contiguous, masked FP8 NT GEMM"
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+HEADLINE = 1                 # dense 4096x7168x2048
+KERNEL_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_amd", "csrc", "dg_kernel.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse_args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--only", type=int, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload_name: str):
+    """HBM bytes per launch from the committed counter summary of this
+    workload, or None if there is none or the kernel source changed since."""
+    path = os.path.join(PROFILES, f"traffic_{workload_name}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_sha():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_workload(w, steps: int, warmup: int):
+    import torch
+    from moe_grouped_gemm_amd import dg
+
+    d = w.new_output()
+    for _ in range(warmup):
+        dg.run_workload(w, d)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        dg.run_workload(w, d)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = start.elapsed_time(end) / steps
+    return wall * 1e3 / steps, kernel_ms
+
+
+def cpu_baseline(w, budget_s: float = 20.0):
+    """The oracle timed on this host on the same bytes (full workload,
+    repeated while within the time budget)."""
+    import numpy as np
+    from moe_grouped_gemm_amd import synth
+    from oracle import dg_oracle as O
+
+    a, sfa, b, sfb = (synth.to_numpy_bytes(t) for t in (w.a, w.sfa, w.b, w.sfb))
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            threads = int(infos[0]["num_threads"])
+    except Exception:
+        pass
+    runs, t_total = 0, 0.0
+    while runs == 0 or (t_total < budget_s / 2 and runs < 5):
+        t0 = time.perf_counter()
+        O.fp8_gemm_nt(a, sfa, b, sfb)
+        t_total += time.perf_counter() - t0
+        runs += 1
+    sec = t_total / runs
+    return {
+        "value": round(w.flops() / sec / 1e12, 6),
+        "unit": "TFLOPS",
+        "cores": threads if threads else len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"full {w.m}x{w.n}x{w.k} dense workload, {runs} run(s) of the float64 numpy oracle "
+                  f"(dequantise, fp64 GEMM, BF16 rounding), {sec:.2f} s each",
+    }
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": 3}), flush=True)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the GEMM has no cross-GPU step; see the sharding notes in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from moe_grouped_gemm_amd import dg, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    dg.lib()
+    dev = torch.device("cuda:0")
+
+    headline = args.only if args.only is not None else HEADLINE
+    spec = synth.workload_spec(headline)
+    w = synth.make_workload(spec, seed=0, device=dev)
+    torch.cuda.synchronize()
+    ms_step, kernel_ms = time_workload(w, args.steps, args.warmup)
+    flops = w.flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    traffic = read_traffic(spec.name)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "kind": spec.kind, "n": spec.n, "k": spec.k,
+                   **({"m": spec.m} if spec.kind == "dense" else {}),
+                   "accumulate": "fp32 with per-128-K promotion", "output": "bf16", "seed": 0},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "fp8_gemm_nt_kernel", "kernel_ms": round(kernel_ms, 5),
+                     "algorithmic_bytes": w.algorithmic_bytes()},
+    }
+    if spec.kind == "masked":
+        gbs = w.algorithmic_bytes() / (kernel_ms * 1e-3) / 1e9
+        out["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(gbs / HBM_PEAK_GBS, 4)})
+
+    if args.only is None and not args.no_extra:
+        extra = {}
+        for idx in (0, 2, 3, 4):
+            s = synth.workload_spec(idx)
+            wx = synth.make_workload(s, seed=0, device=dev)
+            torch.cuda.synchronize()
+            steps = max(5, args.steps // 2)
+            ms, kms = time_workload(wx, steps, max(2, args.warmup // 2))
+            tf = wx.flops() / (kms * 1e-3) / 1e12
+            gbs = wx.algorithmic_bytes() / (kms * 1e-3) / 1e9
+            extra[s.name] = {"kernel_ms": round(kms, 5), "tflops": round(tf, 2),
+                             "fp8_peak_frac": round(tf / FP8_PEAK_TFLOPS, 4),
+                             "algorithmic_gbs": round(gbs, 1), "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+                             "valid_rows": getattr(wx, "valid_rows", lambda: spec.m)() if s.kind != "dense" else s.m}
+            del wx
+            torch.cuda.empty_cache()
+        out["workloads"] = extra
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w) if spec.kind == "dense" else None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,146 @@
+/*
+ * dg.h - FP8 NT GEMM with fine-grained scaling factors and its M-grouped
+ * (MoE) variants, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (see the "DeepGEMM for PPU" README, "Interfaces > Notices",
+ * "Normal dense GEMMs", "Grouped GEMMs (contiguous layout)" and "Grouped GEMMs
+ * (masked layout)"; scale recipe (1, 128, 128) from the "DeepGEMM
+ * Compatibility Wrapper (deep-gemm)" page, "0.2.7 Compatibility Additions"):
+ *
+ *     Ahat[m][k] = e4m3(A[m][k]) * sfa[k/128][m]
+ *     Bhat[n][k] = e4m3(B[n][k]) * sfb[n/128][k/128]
+ *     D[m][n]    = bf16( sum_k Ahat[m][k] * Bhat[n][k] )
+ *
+ * NT format only: A is row-major [M][K] (K contiguous) and B is the
+ * transposed right-hand side, row-major [N][K]. FP8 is OCP E4M3 (e4m3fn,
+ * max 448). Scales are float32. The LHS scales are stored transposed
+ * ("M-major") with a 16-byte aligned leading dimension
+ * ld_sfa = dg_get_tma_aligned_size(M, 4), i.e. sfa[kb * ld_sfa + m]. D is
+ * row-major BF16 [M][N], rounded to nearest even.
+ *
+ * Accumulation: per 128-wide K block the FP8 products are summed in float32
+ * by the matrix cores; each block's partial sum is then multiplied by
+ * sfa * sfb and added into a float32 total ("promotion"). Results agree
+ * with the exact sum rounded once to BF16 up to float32 summation-order
+ * rounding.
+ *
+ * Ownership: every pointer is caller-owned device memory (HIP). The library
+ * allocates nothing, keeps no reference after the call returns, and never
+ * reads device memory from the host. Each call enqueues one kernel on
+ * `stream` (a hipStream_t; NULL = the null stream) and returns without
+ * synchronising; the calls are safe to capture in a HIP graph.
+ *
+ * Errors: arguments are checked before anything is enqueued; any failure
+ * returns a nonzero dg_status and enqueues nothing. Checked: null pointers,
+ * non-positive N/K/max_m, negative M/G, K % 128, N % 128, contiguous
+ * M % 128, 16-byte alignment of A, B, D and of the scale arrays, and the
+ * size limits below. M == 0 (dense, contiguous) and G == 0 are successful
+ * no-ops. A failed kernel launch returns DG_ERR_LAUNCH. Faults inside a
+ * kernel surface asynchronously at the caller's next synchronisation, as
+ * for any HIP kernel. Thread safety: calls may be made from any thread;
+ * the only library state is the CU-count setting.
+ *
+ * Limits: K <= 2^20, N <= 2^20, every operand < 2^40 bytes, num_groups <= 4096
+ * for the masked layout.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int dg_status;
+
+#define DG_OK 0
+#define DG_ERR_NULL 1         /* a required pointer is NULL                   */
+#define DG_ERR_SHAPE 2        /* a size is out of range or not a multiple     */
+#define DG_ERR_ALIGN 3        /* a pointer is not 16-byte aligned             */
+#define DG_ERR_UNSUPPORTED 4  /* a size beyond the documented limits          */
+#define DG_ERR_LAUNCH 5       /* hipLaunchKernel or a HIP query failed        */
+#define DG_ERR_DEVICE 6       /* no HIP device, or the device is not gfx950   */
+
+/*
+ * Dense FP8 NT GEMM ("DeepGEMM for PPU" README, "Normal dense GEMMs").
+ *   a   [m][k]   E4M3                       b   [n][k]   E4M3
+ *   sfa [k/128][dg_get_tma_aligned_size(m,4)] float32
+ *   sfb [n/128][k/128] float32              d   [m][n]   BF16 (written in full)
+ * m >= 0 (any value; ragged M is supported), n % 128 == 0, k % 128 == 0.
+ */
+dg_status dg_fp8_gemm_nt(const void* a, const float* sfa,
+                         const void* b, const float* sfb,
+                         void* d,
+                         int m, int n, int k, void* stream);
+
+/*
+ * M-grouped FP8 NT GEMM, contiguous layout ("DeepGEMM for PPU" README,
+ * "Grouped GEMMs (contiguous layout)"; 128-row alignment from the
+ * "DeepGEMM Compatibility Wrapper" page, "Contiguous Grouped GEMM
+ * Alignment"). Only M is grouped; N and K are shared by every group.
+ *   a   [m][k] E4M3, the groups' rows concatenated, each group's segment
+ *       starting on a multiple of 128 rows and padded to one
+ *   sfa [k/128][dg_get_tma_aligned_size(m,4)] float32
+ *   b   [num_groups][n][k] E4M3          sfb [num_groups][n/128][k/128] float32
+ *   d   [m][n] BF16
+ *   grouped_layout [m] int32 (device): group id of each row, -1 for padding.
+ * Row r of d is written iff grouped_layout[r] is the id g of the 128-row
+ * block that holds r (the id of the block's first row) and 0 <= g < G.
+ * Padding rows, and whole blocks whose first row has an id outside [0, G),
+ * are never written and never influence written rows. m % 128 == 0.
+ */
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa,
+                                              const void* b, const float* sfb,
+                                              void* d, const int32_t* grouped_layout,
+                                              int m, int n, int k, int num_groups,
+                                              void* stream);
+
+/*
+ * M-grouped FP8 NT GEMM, masked layout ("DeepGEMM for PPU" README,
+ * "Grouped GEMMs (masked layout)"), for decoding under graph capture where
+ * the host does not know how many rows each group holds.
+ *   a   [num_groups][max_m][k] E4M3
+ *   sfa [num_groups][k/128][dg_get_tma_aligned_size(max_m,4)] float32
+ *   b   [num_groups][n][k] E4M3          sfb [num_groups][n/128][k/128] float32
+ *   d   [num_groups][max_m][n] BF16
+ *   masked_m [num_groups] int32 (device): valid rows of each group, read by
+ *       the kernel only, clamped to [0, max_m].
+ * Rows m < masked_m[g] of d[g] are written; all other rows are untouched.
+ * The launch shape depends only on (num_groups, max_m, n, k) and the CU
+ * count, so one captured graph serves any masked_m contents.
+ */
+dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa,
+                                          const void* b, const float* sfb,
+                                          void* d, const int32_t* masked_m,
+                                          int num_groups, int max_m, int n, int k,
+                                          void* stream);
+
+/* Row alignment of each group's segment in the contiguous layout: 128
+ * ("DeepGEMM Compatibility Wrapper" page, "Contiguous Grouped GEMM
+ * Alignment"; "DeepGEMM for PPU" README, "Utilities"). */
+int dg_get_mk_alignment_for_contiguous_layout(void);
+
+/* x rounded up so that x * element_size is a multiple of 16 bytes: the
+ * leading dimension of the transposed LHS scales ("DeepGEMM for PPU"
+ * README, "Utilities"; "DeepGEMM Compatibility Wrapper" page, "0.2.7
+ * Compatibility Additions"). Returns -1 for x < 0 or an element_size that
+ * does not divide 16. */
+int dg_get_tma_aligned_size(int x, int element_size);
+
+/* Number of compute units the persistent kernels spread over ("DeepGEMM for
+ * PPU" README, "Utilities": the maximum SM count to use). Defaults to all
+ * CUs of the current device. dg_get_num_cus returns 0 when there is no
+ * device. dg_set_num_cus(n) with n <= 0 restores the default; n above the
+ * device's CU count is clamped to it. */
+int dg_get_num_cus(void);
+dg_status dg_set_num_cus(int num_cus);
+
+/* Static description of a status code. */
+const char* dg_status_string(dg_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H */

@@ -1,0 +1,202 @@
+"""Python binding of libdg.so: the FP8 NT GEMM and its M-grouped variants.
+
+Argument marshalling only: each function checks tensor dtypes, shapes,
+devices and contiguity, then passes raw device pointers and the current HIP
+stream to the C ABI declared in include/dg.h. All arithmetic runs in the
+library's gfx950 kernels. There is no fallback: a missing library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdg.so")
+
+DG_OK = 0
+_STATUS_NAMES = {0: "DG_OK", 1: "DG_ERR_NULL", 2: "DG_ERR_SHAPE", 3: "DG_ERR_ALIGN",
+                 4: "DG_ERR_UNSUPPORTED", 5: "DG_ERR_LAUNCH", 6: "DG_ERR_DEVICE"}
+
+# (name, argtypes, restype) of every symbol include/dg.h declares.
+_vp, _i = ctypes.c_void_p, ctypes.c_int
+SIGNATURES = [
+    ("dg_fp8_gemm_nt", [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp], _i),
+    ("dg_m_grouped_fp8_gemm_nt_contiguous", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
+    ("dg_m_grouped_fp8_gemm_nt_masked", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
+    ("dg_get_mk_alignment_for_contiguous_layout", [], _i),
+    ("dg_get_tma_aligned_size", [_i, _i], _i),
+    ("dg_get_num_cus", [], _i),
+    ("dg_set_num_cus", [_i], _i),
+    ("dg_status_string", [_i], ctypes.c_char_p),
+]
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = lib().dg_status_string(status).decode()
+        super().__init__(f"{what}: {_STATUS_NAMES.get(status, status)} ({msg})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use; raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_grouped_gemm_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, argtypes, restype in SIGNATURES:
+            fn = getattr(handle, name)
+            fn.argtypes = argtypes
+            fn.restype = restype
+        _lib = handle
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != DG_OK:
+        raise DGError(status, what)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# Utilities (include/dg.h)
+# ---------------------------------------------------------------------------
+
+def get_mk_alignment_for_contiguous_layout() -> int:
+    return lib().dg_get_mk_alignment_for_contiguous_layout()
+
+
+def get_tma_aligned_size(x: int, element_size: int) -> int:
+    r = lib().dg_get_tma_aligned_size(int(x), int(element_size))
+    if r < 0:
+        raise ValueError(f"bad arguments ({x}, {element_size})")
+    return r
+
+
+def get_num_cus() -> int:
+    return lib().dg_get_num_cus()
+
+
+def set_num_cus(n: int) -> None:
+    _check(lib().dg_set_num_cus(int(n)), "dg_set_num_cus")
+
+
+def get_mn_major_tma_aligned_tensor(sf: torch.Tensor) -> torch.Tensor:
+    """Lays out LHS scales [..., M, K/128] (float32) transposed with an aligned
+    leading dimension: [..., K/128, tma_aligned(M)], the layout the kernels
+    read. Padding entries are zero. (A layout helper; no GEMM arithmetic.)"""
+    *lead, m, kb = sf.shape
+    ld = get_tma_aligned_size(m, 4)
+    out = torch.zeros(*lead, kb, ld, dtype=torch.float32, device=sf.device)
+    out[..., :m] = sf.transpose(-1, -2)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The three GEMMs
+# ---------------------------------------------------------------------------
+
+def fp8_gemm_nt(a, sfa, b, sfb, d) -> torch.Tensor:
+    """d[m, n] = bf16(sum_k a[m,k] sfa[k/128][m] * b[n,k] sfb[n/128][k/128]).
+
+    a [M, K] float8_e4m3fn, sfa [K/128, tma_aligned(M)] float32,
+    b [N, K] float8_e4m3fn, sfb [N/128, K/128] float32, d [M, N] bfloat16.
+    """
+    dev = a.device
+    m, k = a.shape
+    n = b.shape[0]
+    _need(a, "a", torch.float8_e4m3fn, 2, dev)
+    _need(b, "b", torch.float8_e4m3fn, 2, dev)
+    _need(sfa, "sfa", torch.float32, 2, dev)
+    _need(sfb, "sfb", torch.float32, 2, dev)
+    _need(d, "d", torch.bfloat16, 2, dev)
+    if b.shape[1] != k or tuple(d.shape) != (m, n):
+        raise ValueError("shape mismatch between a, b and d")
+    if k % 128 or n % 128:
+        raise ValueError("k and n must be multiples of 128")
+    if tuple(sfa.shape) != (k // 128, get_tma_aligned_size(m, 4)) or tuple(sfb.shape) != (n // 128, k // 128):
+        raise ValueError("scale shapes do not match the (1, 128, 128) recipe layout")
+    _check(lib().dg_fp8_gemm_nt(a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(), d.data_ptr(),
+                                m, n, k, _stream(a)), "dg_fp8_gemm_nt")
+    return d
+
+
+def m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, grouped_layout) -> torch.Tensor:
+    """Contiguous-layout grouped GEMM; grouped_layout [M] int32 holds each
+    row's group (-1 for padding). b [G, N, K], sfb [G, N/128, K/128]."""
+    dev = a.device
+    m, k = a.shape
+    g, n, _ = b.shape
+    _need(a, "a", torch.float8_e4m3fn, 2, dev)
+    _need(b, "b", torch.float8_e4m3fn, 3, dev)
+    _need(sfa, "sfa", torch.float32, 2, dev)
+    _need(sfb, "sfb", torch.float32, 3, dev)
+    _need(d, "d", torch.bfloat16, 2, dev)
+    _need(grouped_layout, "grouped_layout", torch.int32, 1, dev)
+    if b.shape[2] != k or tuple(d.shape) != (m, n) or grouped_layout.shape[0] != m:
+        raise ValueError("shape mismatch between a, b, d and grouped_layout")
+    if tuple(sfa.shape) != (k // 128, get_tma_aligned_size(m, 4)) or tuple(sfb.shape) != (g, n // 128, k // 128):
+        raise ValueError("scale shapes do not match the (1, 128, 128) recipe layout")
+    _check(lib().dg_m_grouped_fp8_gemm_nt_contiguous(
+        a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(), d.data_ptr(), grouped_layout.data_ptr(),
+        m, n, k, g, _stream(a)), "dg_m_grouped_fp8_gemm_nt_contiguous")
+    return d
+
+
+def m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, d, masked_m) -> torch.Tensor:
+    """Masked-layout grouped GEMM; masked_m [G] int32 (device) holds each
+    group's valid rows. a [G, max_m, K], sfa [G, K/128, tma_aligned(max_m)],
+    b [G, N, K], sfb [G, N/128, K/128], d [G, max_m, N]."""
+    dev = a.device
+    g, max_m, k = a.shape
+    n = b.shape[1]
+    _need(a, "a", torch.float8_e4m3fn, 3, dev)
+    _need(b, "b", torch.float8_e4m3fn, 3, dev)
+    _need(sfa, "sfa", torch.float32, 3, dev)
+    _need(sfb, "sfb", torch.float32, 3, dev)
+    _need(d, "d", torch.bfloat16, 3, dev)
+    _need(masked_m, "masked_m", torch.int32, 1, dev)
+    if b.shape[0] != g or b.shape[2] != k or tuple(d.shape) != (g, max_m, n) or masked_m.shape[0] != g:
+        raise ValueError("shape mismatch between a, b, d and masked_m")
+    if (tuple(sfa.shape) != (g, k // 128, get_tma_aligned_size(max_m, 4))
+            or tuple(sfb.shape) != (g, n // 128, k // 128)):
+        raise ValueError("scale shapes do not match the (1, 128, 128) recipe layout")
+    _check(lib().dg_m_grouped_fp8_gemm_nt_masked(
+        a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(), d.data_ptr(), masked_m.data_ptr(),
+        g, max_m, n, k, _stream(a)), "dg_m_grouped_fp8_gemm_nt_masked")
+    return d
+
+
+def run_workload(w, d: torch.Tensor) -> torch.Tensor:
+    """Runs the GEMM that matches a synth workload (Dense / Contiguous / Masked)."""
+    kind = type(w).__name__
+    if kind == "Dense":
+        return fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d)
+    if kind == "Contiguous":
+        return m_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout)
+    if kind == "Masked":
+        return m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m)
+    raise TypeError(kind)

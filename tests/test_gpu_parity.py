@@ -1,0 +1,291 @@
+"""GPU parity: the gfx950 kernels against the CPU oracle, through the C ABI.
+
+Small shapes (several tiles, ragged tails, empty groups) are compared in
+full; the five benchmark workloads at full size are compared on sampled
+rows and columns, plus the invariant that no row outside the valid rows is
+written. Integer-exact inputs are compared bit for bit.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from moe_grouped_gemm_amd import dg, synth
+from oracle import dg_oracle as O
+from parity import check_close, check_untouched
+
+pytestmark = pytest.mark.gpu
+
+NP = synth.to_numpy_bytes
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dg.lib()  # the native library must load: no fallback
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Dense
+# ---------------------------------------------------------------------------
+
+DENSE_SHAPES = [
+    (128, 256, 512),     # the small benchmark workload
+    (300, 384, 1024),    # ragged M, 3 N blocks
+    (1, 128, 128),
+    (17, 256, 256),
+    (257, 128, 128),
+    (64, 256, 4096),
+    (1000, 640, 384),
+    (2048, 1024, 1024),  # more tiles than CUs
+]
+
+
+@pytest.mark.parametrize("m,n,k", DENSE_SHAPES)
+def test_dense_small(dev, m, n, k):
+    _say(f"dense {m}x{n}x{k}")
+    w = synth.make_dense(m, n, k, seed=m + n + k, device=dev)
+    d = w.new_output()
+    dg.fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d)
+    torch.cuda.synchronize()
+    ref = O.gemm_nt_f64(NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb))
+    check_close(NP(d), ref, f"dense {m}x{n}x{k}")
+
+
+CODE_OF = {0: 0x00, 1: 0x38, 2: 0x40, -1: 0xB8, -2: 0xC0}
+
+
+def _int_exact(m, n, k, seed):
+    """Codes in {-2..2} and power-of-two scales varying per K block, row and
+    N block: every float32 partial and promoted sum is exact."""
+    rng = np.random.default_rng(seed)
+    lut = np.zeros(5, np.uint8)
+    for v, c in CODE_OF.items():
+        lut[v + 2] = c
+    a = lut[rng.integers(-2, 3, size=(m, k)) + 2]
+    b = lut[rng.integers(-2, 3, size=(n, k)) + 2]
+    ld = (m + 3) // 4 * 4
+    sfa = np.ldexp(1.0, rng.integers(-2, 3, size=(k // 128, ld))).astype(np.float32)
+    sfb = np.ldexp(1.0, rng.integers(-2, 3, size=(n // 128, k // 128))).astype(np.float32)
+    return a, sfa, b, sfb
+
+
+def _dev_fp8(x, dev):
+    return torch.from_numpy(x).to(dev).view(torch.float8_e4m3fn)
+
+
+@pytest.mark.parametrize("m,n,k", [(200, 256, 1024), (129, 384, 2048)])
+def test_dense_integer_exact_bitwise(dev, m, n, k):
+    _say(f"dense integer-exact {m}x{n}x{k}")
+    a, sfa, b, sfb = _int_exact(m, n, k, seed=m)
+    d = synth.sentinel_output((m, n), dev)
+    dg.fp8_gemm_nt(_dev_fp8(a, dev), torch.from_numpy(sfa).to(dev), _dev_fp8(b, dev),
+                   torch.from_numpy(sfb).to(dev), d)
+    torch.cuda.synchronize()
+    ref_bits = O.fp8_gemm_nt(a, sfa, b, sfb)
+    got = NP(d)
+    assert np.array_equal(got, ref_bits), f"{np.sum(got != ref_bits)} mismatching elements"
+
+
+def test_dense_deterministic(dev):
+    w = synth.make_dense(1024, 2048, 1024, seed=5, device=dev)
+    d1, d2 = w.new_output(), w.new_output()
+    dg.fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d1)
+    dg.fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d2)
+    torch.cuda.synchronize()
+    assert torch.equal(d1.view(torch.int16), d2.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Contiguous layout
+# ---------------------------------------------------------------------------
+
+def _contig_ref(w):
+    return O.m_grouped_fp8_gemm_nt_contiguous(NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb), NP(w.layout),
+                                              np.full((w.m, w.n), 0xFFFF, np.uint16))
+
+
+def _check_contiguous(w, d, what):
+    got = NP(d)
+    layout = NP(w.layout)
+    valid = layout >= 0
+    ref = np.full((w.m, w.n), np.nan)
+    for g in range(w.num_groups):
+        rows = np.nonzero(layout == g)[0]
+        if rows.size:
+            ref[rows] = O.dense_f64_at(NP(w.a), NP(w.sfa), NP(w.b)[g], NP(w.sfb)[g], rows, np.arange(w.n))
+    check_close(got[valid], ref[valid], what)
+    check_untouched(got[~valid], what + " padding rows")
+
+
+@pytest.mark.parametrize("rows,n,k", [
+    ([130, 0, 77, 256, 1], 256, 512),
+    ([128], 128, 128),
+    ([5, 300, 1, 129], 384, 1024),
+])
+def test_contiguous_small(dev, rows, n, k):
+    _say(f"contiguous rows={rows} n={n} k={k}")
+    w = synth.make_contiguous(rows, n, k, seed=len(rows), device=dev, poison_padding=True)
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout)
+    torch.cuda.synchronize()
+    _check_contiguous(w, d, f"contiguous {rows}")
+
+
+def test_contiguous_out_of_range_ids_and_padding_blocks(dev):
+    w = synth.make_contiguous([200, 100, 128], 256, 256, seed=3, device=dev)
+    layout = w.layout.clone()
+    # a whole padding block in the middle and a segment with an id >= G
+    lay = NP(layout).copy()
+    lay[256:384] = -1
+    lay[384:484] = 7
+    lay[484:512] = -1
+    layout.copy_(torch.from_numpy(lay))
+    w.layout = layout
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout)
+    torch.cuda.synchronize()
+    got = NP(d)
+    check_untouched(got[256:], "ids outside [0, G)")
+    ref = O.m_grouped_fp8_gemm_nt_contiguous(NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb), lay,
+                                             np.full((w.m, w.n), 0xFFFF, np.uint16))
+    assert np.all(ref[256:] == 0xFFFF)
+    valid = lay >= 0
+    valid[256:] = False
+    ref64 = np.zeros((int(valid.sum()), w.n))
+    ref64[:] = O.dense_f64_at(NP(w.a), NP(w.sfa), NP(w.b)[0], NP(w.sfb)[0], np.nonzero(valid)[0], np.arange(w.n))
+    check_close(got[valid], ref64, "group 0")
+
+
+def test_contiguous_equals_dense_per_group(dev):
+    """Same kernel arithmetic, so a group's rows match a dense call on them bit for bit."""
+    w = synth.make_contiguous([256, 128, 384], 512, 1024, seed=9, device=dev)
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout)
+    start = 0
+    for g, r in enumerate(w.rows):
+        a_g = w.a[start:start + r].contiguous()
+        sfa_g = w.sfa[:, start:start + r].contiguous()
+        d_g = synth.sentinel_output((r, w.n), dev)
+        dg.fp8_gemm_nt(a_g, sfa_g, w.b[g].contiguous(), w.sfb[g].contiguous(), d_g)
+        torch.cuda.synchronize()
+        assert torch.equal(d[start:start + r].view(torch.int16), d_g.view(torch.int16)), f"group {g}"
+        start += r
+
+
+# ---------------------------------------------------------------------------
+# Masked layout
+# ---------------------------------------------------------------------------
+
+def _check_masked(w, d, counts, what):
+    got = NP(d)
+    for g, c in enumerate(counts):
+        v = min(max(int(c), 0), w.max_m)
+        if v:
+            ref = O.dense_f64_at(NP(w.a)[g], NP(w.sfa)[g], NP(w.b)[g], NP(w.sfb)[g], np.arange(v), np.arange(w.n))
+            check_close(got[g, :v], ref, f"{what} group {g}")
+        check_untouched(got[g, v:], f"{what} group {g} rows >= {v}")
+
+
+@pytest.mark.parametrize("counts,max_m,n,k", [
+    ([0, 1, 200, 77], 200, 256, 512),
+    ([256, 129], 256, 384, 1024),
+    ([3], 64, 128, 128),
+])
+def test_masked_small(dev, counts, max_m, n, k):
+    _say(f"masked counts={counts} max_m={max_m} n={n} k={k}")
+    w = synth.make_masked(counts, max_m, n, k, seed=max_m, device=dev, poison_invalid=True)
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m)
+    torch.cuda.synchronize()
+    _check_masked(w, d, counts, "masked")
+
+
+def test_masked_clamps_counts(dev):
+    w = synth.make_masked([10, 10, 10], 96, 128, 256, seed=1, device=dev)
+    w.masked_m.copy_(torch.tensor([-3, 500, 33], dtype=torch.int32))
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m)
+    torch.cuda.synchronize()
+    _check_masked(w, d, [-3, 500, 33], "clamped")
+
+
+def test_masked_graph_replay_follows_device_counts(dev):
+    """One captured graph serves changing masked_m contents; replays are
+    checked against eager calls, with eager work between replays."""
+    w = synth.make_masked([40, 100, 7, 64], 128, 256, 512, seed=2, device=dev)
+    d = w.new_output()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        dg.m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m)  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dg.m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m)
+    for counts in ([40, 100, 7, 64], [128, 0, 1, 127], [5, 5, 5, 5]):
+        w.masked_m.copy_(torch.tensor(counts, dtype=torch.int32))
+        d.view(torch.int16).fill_(-1)
+        graph.replay()
+        torch.cuda.synchronize()
+        d_eager = w.new_output()
+        dg.m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d_eager, w.masked_m)
+        torch.cuda.synchronize()
+        assert torch.equal(d.view(torch.int16), d_eager.view(torch.int16)), counts
+        _check_masked(w, d, counts, f"graph {counts}")
+
+
+# ---------------------------------------------------------------------------
+# The five benchmark workloads at full size (sampled comparison)
+# ---------------------------------------------------------------------------
+
+def _sample(n_total, count, rng, extra=()):
+    idx = set(int(x) for x in rng.choice(n_total, size=min(count, n_total), replace=False))
+    idx.update(int(e) for e in extra if 0 <= e < n_total)
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+@pytest.mark.parametrize("index", [0, 1, 2, 3, 4])
+def test_workload_full_size(dev, index):
+    spec = synth.workload_spec(index)
+    _say(f"workload {index} {spec.name}")
+    w = synth.make_workload(spec, seed=0, device=dev)
+    d = w.new_output()
+    dg.run_workload(w, d)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(100 + index)
+    got = NP(d)
+    a, sfa, b, sfb = NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb)
+    if spec.kind == "dense":
+        rows = _sample(w.m, 96, rng, (0, 127, 128, 255, 256, w.m - 1))
+        cols = _sample(w.n, 96, rng, (0, 127, 128, 255, w.n - 1))
+        ref = O.dense_f64_at(a, sfa, b, sfb, rows, cols)
+        check_close(got[np.ix_(rows, cols)], ref, spec.name)
+    elif spec.kind == "contiguous":
+        layout = NP(w.layout)
+        valid_rows = np.nonzero(layout >= 0)[0]
+        starts = np.nonzero(np.diff(np.r_[-2, layout]) != 0)[0]
+        rows = np.union1d(valid_rows[rng.choice(valid_rows.size, 128, replace=False)],
+                          np.intersect1d(starts, valid_rows))
+        cols = _sample(w.n, 64, rng, (0, 127, 128, w.n - 1))
+        ref = O.contiguous_f64_at(a, sfa, b, sfb, layout, rows, cols)
+        check_close(got[np.ix_(rows, cols)], ref, spec.name)
+        check_untouched(got[layout < 0], spec.name + " padding rows")
+    else:
+        counts = w.counts
+        for g in range(w.num_groups):
+            v = counts[g]
+            rows = _sample(v, 8, rng, (0, v - 1))
+            cols = _sample(w.n, 32, rng, (0, w.n - 1))
+            ref = O.masked_f64_at(a, sfa, b, sfb, w.masked_m.cpu().numpy(), g, rows, cols)
+            check_close(got[g][np.ix_(rows, cols)], ref, f"{spec.name} group {g}")
+            check_untouched(got[g, v:], f"{spec.name} group {g} rows >= {v}")
