@@ -128,8 +128,39 @@ struct TileRef {
   uint16_t* d;         // row 0 of the group's D
   int group;
   int m0, n0;          // first row (within the group) and column of the tile
-  int row_limit;       // rows >= row_limit are not addressable (loads clamp)
-  int valid_rows;      // dense / masked: rows < valid_rows are written
+  int load_rows;       // A rows at or beyond this are not loaded (they read as zero)
+  int valid_rows;      // dense / masked: rows below this are written
+  bool active;         // false: no such tile (past the end, or nothing to compute)
+};
+
+// Raw buffer descriptor (gfx9 word 3: 32-bit data format). Loads at byte
+// offsets at or beyond `bytes` return zero without touching memory.
+// The caller guarantees that base and bytes are the same in every lane; they
+// are moved to scalar registers so that the descriptor is scalar.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// One wave-wide 16-byte buffer load per lane into LDS: lane l writes
+// lds_base + 16 * l (lds_base is the same for the whole wave).
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void buf_dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 4, voff, 0, 0, 0);
+}
+
+// Per-lane byte offsets of this lane's loads within a tile, fixed for the
+// kernel: row * K + 16 * chunk for the A and B tile loads (the j-th load of a
+// wave adds j * NW * 8 rows), and 4 * row for the scale load.
+struct LaneOffsets {
+  uint32_t ab;
+  uint32_t ab_step;    // bytes between a wave's consecutive tile loads
+  uint32_t sa;
 };
 
 // Maps a linear tile index to (m block, n block), walking panels of
@@ -151,49 +182,156 @@ struct Config {
   static constexpr int THREADS = NW * 64;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int MT = WM / 16, NT = WN / 16;
+  static constexpr int SLOTS = BM / 128;  // contiguous layout: 128-row segment blocks per tile row block
   static constexpr int A_DMA = BM * ROW_BYTES / 1024 / NW;  // 1 KB per wave-wide 16-byte load
   static constexpr int B_DMA = BN * ROW_BYTES / 1024 / NW;
-  static constexpr int SA_DMA = WM / 64;                    // 256 B (64 scales) per wave-wide 4-byte load
-  static constexpr int LOADS_PER_STAGE = A_DMA + B_DMA + SA_DMA;
+  // LHS scales: wave w loads rows [w * SA_ROWS, w * SA_ROWS + 64) of the tile
+  // into its own 256-byte region; row r is read from region r / SA_ROWS.
+  static constexpr int SA_ROWS = BM / NW;
+  // Per stage and wave: A and B tile loads, one scale load, the RHS scale.
+  static constexpr int LOADS_PER_STAGE = A_DMA + B_DMA + 1 + 1;
   static constexpr int A_BYTES = BM * ROW_BYTES, B_BYTES = BN * ROW_BYTES;
-  static constexpr int SA_BYTES = NW * WM * 4;
+  static constexpr int SA_BYTES = NW * 256;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static_assert(BM % 128 == 0, "tile rows are whole 128-row blocks");
   static_assert(BM % (WAVES_M * 16) == 0 && BN % (WAVES_N * 16) == 0, "wave tile");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns lie in one 128-column scale block");
   static_assert(BM * ROW_BYTES % (1024 * NW) == 0 && BN * ROW_BYTES % (1024 * NW) == 0, "DMA split");
-  static_assert(WM % 64 == 0, "scale DMA granularity");
+  static_assert(SA_ROWS <= 64 && BM % NW == 0, "scale load granularity");
 };
 
+// Resolves linear tile index t of layout KIND. Tile order:
+//   dense:      raster over (M block, N block);
+//   contiguous: slot-major, then raster over (BM-row block, N block); slot j
+//               of a block is the j-th distinct valid group among its 128-row
+//               segment blocks (a block holds two groups only where a group's
+//               segment ends inside it), so slot 0 carries nearly all work;
+//   masked:     per group (prefix sums of the per-group tile counts, read
+//               from masked_m on the device), then N block, then M block.
+template <class C, int KIND>
+__device__ __forceinline__ TileRef resolve_tile(const GemmArgs& p, int t, int num_tiles, const int* s_prefix) {
+  TileRef tr;
+  tr.active = false;
+  if (t >= num_tiles) return tr;
+  const size_t K = (size_t)p.k;
+  const int k_blocks = p.k / BK;
+  if constexpr (KIND == KIND_MASKED) {
+    int lo = 0, hi = p.num_groups - 1;  // last g with prefix[g] <= t: a group with tiles
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_prefix[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo;
+    const int v = min(max(p.aux[g], 0), p.m);
+    const int mblocks = (v + C::BM - 1) / C::BM;
+    const int local = t - s_prefix[g];
+    const int nb = local / mblocks;
+    const int mb = local - nb * mblocks;
+    tr.group = g;
+    tr.a = p.a + (size_t)g * p.m * K;
+    tr.sfa = p.sfa + (size_t)g * k_blocks * p.ld_sfa;
+    tr.b = p.b + (size_t)g * p.n * K;
+    tr.sfb = p.sfb + (size_t)g * (p.n / BK) * k_blocks;
+    tr.d = p.d + (size_t)g * p.m * p.n;
+    tr.m0 = mb * C::BM;
+    tr.n0 = nb * C::BN;
+    tr.load_rows = v;        // rows past masked_m are never fetched
+    tr.valid_rows = v;
+    tr.active = true;
+  } else {
+    const int per_slot = p.m_blocks * p.n_blocks;
+    const int slot = t / per_slot;
+    int mb, nb;
+    raster(t - slot * per_slot, p.m_blocks, p.n_blocks, 8, mb, nb);
+    tr.m0 = mb * C::BM;
+    tr.n0 = nb * C::BN;
+    tr.load_rows = p.m;
+    tr.valid_rows = p.m;
+    tr.a = p.a;
+    tr.sfa = p.sfa;
+    tr.d = p.d;
+    tr.group = 0;
+    tr.b = p.b;
+    tr.sfb = p.sfb;
+    if constexpr (KIND == KIND_CONTIGUOUS) {
+      // The distinct valid groups of this block's 128-row segment blocks, in order.
+      int found = 0, g_sel = -1;
+#pragma unroll
+      for (int j = 0; j < C::SLOTS; ++j) {
+        const int r = tr.m0 + 128 * j;
+        const int g = r < p.m ? p.aux[r] : -1;
+        bool fresh = g >= 0 && g < p.num_groups;
+#pragma unroll
+        for (int i = 0; i < j; ++i) {
+          const int ri = tr.m0 + 128 * i;
+          if (ri < p.m && p.aux[ri] == g) fresh = false;
+        }
+        if (fresh) {
+          if (found == slot) g_sel = g;
+          ++found;
+        }
+      }
+      if (g_sel < 0) return tr;  // nothing for this slot: inactive
+      tr.group = g_sel;
+      tr.b = p.b + (size_t)g_sel * p.n * K;
+      tr.sfb = p.sfb + (size_t)g_sel * (p.n / BK) * k_blocks;
+    }
+    tr.active = true;
+  }
+  return tr;
+}
+
+// The first active tile at or after t in this CTA's sequence t, t+grid, ...
+template <class C, int KIND>
+__device__ __forceinline__ TileRef next_active(const GemmArgs& p, int& t, int grid, int num_tiles,
+                                               const int* s_prefix) {
+  for (; t < num_tiles; t += grid) {
+    TileRef tr = resolve_tile<C, KIND>(p, t, num_tiles, s_prefix);
+    if (tr.active) return tr;
+  }
+  TileRef none;
+  none.active = false;
+  return none;
+}
+
+template <class C>
+__device__ __forceinline__ LaneOffsets lane_offsets(int k, int wave, int lane) {
+  LaneOffsets o;
+  const int row0 = wave * 8 + (lane >> 3);
+  const int c = (lane & 7) ^ ((row0 >> 1) & 7);  // the same for every load of the wave (NW * 8 % 16 == 0)
+  o.ab = (uint32_t)row0 * (uint32_t)k + (uint32_t)c * 16u;
+  o.ab_step = (uint32_t)(C::NW * 8) * (uint32_t)k;
+  o.sa = (uint32_t)(wave * C::SA_ROWS + lane) * 4u;
+  return o;
+}
+
 // Loads of K block `kb` of one tile into stage S: the A and B tile rows with
-// the swizzle of lds_offset(), and each wave's own copy of its rows' scales.
+// the swizzle of lds_offset() (rows past the tile's valid rows read as zero),
+// the tile's LHS scales, and the RHS scale of this wave's columns (returned
+// in a register once the loads have landed).
 template <class C, int S>
-__device__ __forceinline__ void issue_stage(const TileRef& tr, int kb, size_t K, int ld_sfa, int wave, int wm0,
-                                            int lane) {
+__device__ __forceinline__ float issue_stage(const TileRef& tr, int kb, const GemmArgs& p, int wave, int wn0,
+                                             const LaneOffsets& lo) {
+  static_assert(C::NW * 8 % 16 == 0, "swizzle phase");
   uint8_t* st = stage_buf<C, S>();
-  const size_t kofs = (size_t)kb * BK;
+  const uint32_t K = (uint32_t)p.k;
+  const int k_blocks = p.k / BK;
+  const uint32_t a_rows = (uint32_t)min(max(tr.load_rows - tr.m0, 0), C::BM);
+  const uint32_t b_rows = (uint32_t)min(p.n - tr.n0, C::BN);
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(tr.a + (size_t)tr.m0 * K + (size_t)kb * BK, a_rows * K);
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(tr.b + (size_t)tr.n0 * K + (size_t)kb * BK, b_rows * K);
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(tr.sfa + (size_t)kb * p.ld_sfa + tr.m0, a_rows * 4u);
 #pragma unroll
-  for (int j = 0; j < C::A_DMA; ++j) {
-    const int blk = j * C::NW + wave;  // which 1 KB (8 rows) of the A tile
-    const int slot = blk * 64 + lane;
-    const int row = slot >> 3;
-    const int c = (slot & 7) ^ ((row >> 1) & 7);
-    const int grow = min(tr.m0 + row, tr.row_limit - 1);
-    dma16(tr.a + (size_t)grow * K + kofs + c * 16, st + blk * 1024);
-  }
+  for (int j = 0; j < C::A_DMA; ++j) buf_dma16(ra, lo.ab + j * lo.ab_step, st + (j * C::NW + wave) * 1024);
 #pragma unroll
-  for (int j = 0; j < C::B_DMA; ++j) {
-    const int blk = j * C::NW + wave;
-    const int slot = blk * 64 + lane;
-    const int row = slot >> 3;
-    const int c = (slot & 7) ^ ((row >> 1) & 7);
-    dma16(tr.b + (size_t)(tr.n0 + row) * K + kofs + c * 16, st + C::A_BYTES + blk * 1024);
-  }
-#pragma unroll
-  for (int j = 0; j < C::SA_DMA; ++j) {
-    const int r = min(tr.m0 + wm0 + j * 64 + lane, tr.row_limit - 1);
-    dma4(tr.sfa + (size_t)kb * ld_sfa + r, st + C::A_BYTES + C::B_BYTES + (wave * C::WM + j * 64) * 4);
-  }
+  for (int j = 0; j < C::B_DMA; ++j)
+    buf_dma16(rb, lo.ab + j * lo.ab_step, st + C::A_BYTES + (j * C::NW + wave) * 1024);
+  buf_dma4(rs, lo.sa, st + C::A_BYTES + C::B_BYTES + wave * 256);
+  const float* sfb_row = tr.sfb + (size_t)((min(tr.n0 + wn0, p.n - 1)) / BK) * k_blocks;
+  const uint32_t bits =
+      __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(sfb_row, (uint32_t)k_blocks * 4u), (uint32_t)kb * 4u, 0, 0);
+  return __builtin_bit_cast(float, bits);
 }
 
 // Wait until this wave's loads of the stage about to be read have landed,
@@ -209,9 +347,102 @@ __device__ __forceinline__ void wait_stage(int ahead) {
   wait_vmcnt_0();
 }
 
+// Position of tile row r's LHS scale in a stage's scale area.
+template <class C>
+__device__ __forceinline__ int sa_index(int r) {
+  return (r / C::SA_ROWS) * 64 + r % C::SA_ROWS;
+}
+
+// Per-wave state of the tile being computed.
+template <class C>
+struct WaveTile {
+  f32x4 acc[C::MT][C::NT];
+  bool row_ok[C::MT];
+  bool on;  // the wave has a valid row and valid columns: it runs its MFMAs and stores
+};
+
+// The K loop of one tile, with global K steps counted from stage PHASE. Each
+// step waits for its stage, refills the stage freed by the previous step with
+// the block STAGES-1 steps ahead (from the next tile once this one runs out),
+// and computes one 128-wide K block.
+template <class C, int KIND, int PHASE>
+__device__ __forceinline__ void mainloop(const GemmArgs& p, const TileRef& cur, const TileRef& nxt,
+                                         WaveTile<C>& wt, float& sb_next, int wave, int wm0, int wn0, int lane,
+                                         const LaneOffsets& lo) {
+  const int k_blocks = p.k / BK;
+  for (int kb0 = 0; kb0 < k_blocks; kb0 += C::STAGES) {
+    static_for<0, C::STAGES>([&](auto si) {
+      constexpr int step = decltype(si)::value;
+      constexpr int s = (step + PHASE) % C::STAGES;
+      const int kb = kb0 + step;
+      if (kb >= k_blocks) return;
+      wait_stage<C>(C::STAGES - 2);
+      wait_lgkmcnt_0();
+      barrier();
+      float sb;
+      // Refill the stage every wave finished reading in the previous step.
+      // Past the end of this tile the loads belong to the next one; with no
+      // next tile the last block is loaded again (nobody reads it): the
+      // loads are issued unconditionally, since a branch here would make the
+      // compiler wait for them before reading the current stage.
+      {
+        const int ahead = kb + C::STAGES - 1;
+        const bool own = ahead < k_blocks;
+        const TileRef& src = (own || !nxt.active) ? cur : nxt;
+        const int kb_load = own ? ahead : (nxt.active ? ahead - k_blocks : k_blocks - 1);
+        const float sb_loaded = issue_stage<C, (s + C::STAGES - 1) % C::STAGES>(src, kb_load, p, wave, wn0, lo);
+        sb = sb_next;          // this step's RHS scale, loaded with its stage
+        sb_next = sb_loaded;
+      }
+      if (!wt.on) return;
+
+      const uint8_t* As = stage_buf<C, s>();
+      const uint8_t* Bs = As + C::A_BYTES;
+      const float* SAs = reinterpret_cast<const float*>(As + C::A_BYTES + C::B_BYTES);
+
+      // Pipeline over the wave's 16-row bands: the next band's A fragment and
+      // scale are read while this band's MFMAs run; each band's partial sums
+      // are promoted right after its MFMAs (the other wave on the SIMD keeps
+      // the matrix core busy meanwhile).
+      i32x8 bf[C::NT];
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt) bf[nt] = read_frag(Bs, wn0 + nt * 16 + (lane & 15), lane);
+      i32x8 af = read_frag(As, wm0 + (lane & 15), lane);
+      float sa = SAs[sa_index<C>(wm0 + (lane & 15))];
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
+        i32x8 af_next;
+        float sa_next = 0.f;
+        if (mt + 1 < C::MT) {
+          af_next = read_frag(As, wm0 + (mt + 1) * 16 + (lane & 15), lane);
+          sa_next = SAs[sa_index<C>(wm0 + (mt + 1) * 16 + (lane & 15))];
+        }
+        f32x4 part[C::NT];
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt)
+          part[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af, (f32x4){0.f, 0.f, 0.f, 0.f}, 0,
+                                                                     0, 0, 0, 0, 0);
+        const float w = sa * sb;
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) wt.acc[mt][nt] += part[nt] * w;
+        if (mt + 1 < C::MT) {
+          af = af_next;
+          sa = sa_next;
+        }
+        // Issue order: the next band's reads first, then the MFMAs, then the
+        // promotion of this band.
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, C::NT, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4 * C::NT + 1, 0);  // VALU
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+  }
+}
+
 template <class C, int KIND>
 __global__ void __launch_bounds__(C::THREADS, 1) fp8_gemm_nt_kernel(GemmArgs p) {
-  static_assert(C::STAGES >= 2 && C::STAGES <= 4, "pipeline depth");
+  static_assert(C::STAGES == 2, "the cross-tile refill assumes one stage in flight");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar scale loads
@@ -220,7 +451,6 @@ __global__ void __launch_bounds__(C::THREADS, 1) fp8_gemm_nt_kernel(GemmArgs p) 
   const int wm0 = wave_m * C::WM;
   const int wn0 = wave_n * C::WN;
   const int k_blocks = p.k / BK;
-  const size_t K = (size_t)p.k;
 
   // Per-group tile counts for the masked layout, read on the device.
   int num_tiles = p.num_tiles;
@@ -247,147 +477,64 @@ __global__ void __launch_bounds__(C::THREADS, 1) fp8_gemm_nt_kernel(GemmArgs p) 
   int rank = blockIdx.x;
   if ((grid & 7) == 0) rank = (blockIdx.x & 7) * (grid >> 3) + (blockIdx.x >> 3);
 
-  for (int t = rank; t < num_tiles; t += grid) {
-    TileRef tr;
-    if constexpr (KIND == KIND_MASKED) {
-      int lo = 0, hi = p.num_groups - 1;  // last g with prefix[g] <= t
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_prefix[mid] <= t) lo = mid; else hi = mid - 1;
-      }
-      const int g = lo;
-      const int v = min(max(p.aux[g], 0), p.m);
-      const int mblocks = (v + C::BM - 1) / C::BM;
-      const int local = t - s_prefix[g];
-      const int nb = local / mblocks;
-      const int mb = local - nb * mblocks;
-      tr.group = g;
-      tr.a = p.a + (size_t)g * p.m * K;
-      tr.sfa = p.sfa + (size_t)g * k_blocks * p.ld_sfa;
-      tr.b = p.b + (size_t)g * p.n * K;
-      tr.sfb = p.sfb + (size_t)g * (p.n / BK) * k_blocks;
-      tr.d = p.d + (size_t)g * p.m * p.n;
-      tr.m0 = mb * C::BM;
-      tr.n0 = nb * C::BN;
-      tr.row_limit = p.m;
-      tr.valid_rows = v;
-    } else {
-      int mb, nb;
-      raster(t, p.m_blocks, p.n_blocks, 8, mb, nb);
-      tr.m0 = mb * C::BM;
-      tr.n0 = nb * C::BN;
-      tr.row_limit = p.m;
-      tr.valid_rows = p.m;
-      tr.a = p.a;
-      tr.sfa = p.sfa;
-      tr.d = p.d;
-      tr.group = 0;
-      if constexpr (KIND == KIND_CONTIGUOUS) {
-        const int g = p.aux[tr.m0];
-        if (g < 0 || g >= p.num_groups) continue;  // a padding block: nothing to compute or write
-        tr.group = g;
-        tr.b = p.b + (size_t)g * p.n * K;
-        tr.sfb = p.sfb + (size_t)g * (p.n / BK) * k_blocks;
-      } else {
-        tr.b = p.b;
-        tr.sfb = p.sfb;
-      }
-    }
+  int t = rank;
+  TileRef cur = next_active<C, KIND>(p, t, grid, num_tiles, s_prefix);
+  if (!cur.active) return;
+  const LaneOffsets lo = lane_offsets<C>(p.k, wave, lane);
+  // Prologue: the first K block of the first tile into stage 0.
+  float sb_next = issue_stage<C, 0>(cur, 0, p, wave, wn0, lo);
+  int phase = 0;
 
-    // Which of this lane's rows are written, and which 16-row bands of this
-    // wave hold any written row (bands without one skip their MFMAs).
-    bool row_ok[C::MT];
+  WaveTile<C> wt;
+  while (cur.active) {
+    int t_next = t + grid;
+    const TileRef nxt = next_active<C, KIND>(p, t_next, grid, num_tiles, s_prefix);
+
     bool any_row = false;
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) {
-      const int r = tr.m0 + wm0 + mt * 16 + (lane & 15);
+      const int r = cur.m0 + wm0 + mt * 16 + (lane & 15);
       bool ok;
-      if constexpr (KIND == KIND_CONTIGUOUS) ok = (r < p.m) && (p.aux[r] == tr.group);
-      else ok = r < tr.valid_rows;
-      row_ok[mt] = ok;
+      if constexpr (KIND == KIND_CONTIGUOUS) ok = (r < p.m) && (p.aux[r] == cur.group);
+      else ok = r < cur.valid_rows;
+      wt.row_ok[mt] = ok;
       any_row |= ok;
     }
-    // A wave whose rows are all invalid skips its MFMAs (it still takes part
-    // in the loads and barriers).
-    const bool wave_on = __builtin_amdgcn_ballot_w64(any_row) != 0;
-
-    f32x4 acc[C::MT][C::NT];
+    wt.on = (__builtin_amdgcn_ballot_w64(any_row) != 0) && (cur.n0 + wn0 < p.n);
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt) acc[mt][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < C::NT; ++nt) wt.acc[mt][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // The previous tile's stores and stage reads are complete before the
-    // stages are refilled.
-    wait_vmcnt_0();
-    wait_lgkmcnt_0();
-    barrier();
-    static_for<0, C::STAGES - 1>([&](auto si) {
-      constexpr int s = decltype(si)::value;
-      if (s < k_blocks) issue_stage<C, s>(tr, s, K, p.ld_sfa, wave, wm0, lane);
-    });
-
-    const const_f32_ptr sfb_row = uniform_const_ptr(tr.sfb + (size_t)((tr.n0 + wn0) / BK) * k_blocks);
-
-    for (int kb0 = 0; kb0 < k_blocks; kb0 += C::STAGES) {
-      static_for<0, C::STAGES>([&](auto si) {
-        constexpr int s = decltype(si)::value;
-        const int kb = kb0 + s;
-        if (kb >= k_blocks) return;
-        wait_stage<C>(C::STAGES - 2);
-        wait_lgkmcnt_0();
-        barrier();
-        // Refill the stage every wave finished reading in the previous step.
-        // Near the end of K the last block is loaded again instead of
-        // branching around the loads: the stage is not read, and a branch
-        // here would make the compiler wait for these loads before reading
-        // the current stage.
-        issue_stage<C, (s + C::STAGES - 1) % C::STAGES>(tr, min(kb + C::STAGES - 1, k_blocks - 1), K, p.ld_sfa, wave,
-                                                        wm0, lane);
-
-        const uint8_t* As = stage_buf<C, s>();
-        const uint8_t* Bs = As + C::A_BYTES;
-        const float* SAs = reinterpret_cast<const float*>(As + C::A_BYTES + C::B_BYTES) + wave * C::WM;
-        const float sb = sfb_row[kb];
-
-        if (!wave_on) return;
-        i32x8 bf[C::NT];
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) bf[nt] = read_frag(Bs, wn0 + nt * 16 + (lane & 15), lane);
-
-#pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) {
-          const i32x8 af = read_frag(As, wm0 + mt * 16 + (lane & 15), lane);
-          const float w = SAs[mt * 16 + (lane & 15)] * sb;
-          f32x4 part[C::NT];
-#pragma unroll
-          for (int nt = 0; nt < C::NT; ++nt)
-            part[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af, (f32x4){0.f, 0.f, 0.f, 0.f}, 0,
-                                                                       0, 0, 0, 0, 0);
-#pragma unroll
-          for (int nt = 0; nt < C::NT; ++nt) acc[mt][nt] += part[nt] * w;
-        }
-      });
+    if constexpr (C::STAGES == 2) {
+      if (phase == 0) mainloop<C, KIND, 0>(p, cur, nxt, wt, sb_next, wave, wm0, wn0, lane, lo);
+      else mainloop<C, KIND, 1>(p, cur, nxt, wt, sb_next, wave, wm0, wn0, lane, lo);
     }
+    phase = (phase + k_blocks) % C::STAGES;
 
-    // Epilogue: BF16 round-to-nearest-even, 8-byte stores of valid rows.
+    // Epilogue (the next tile's first K block is already in flight): BF16
+    // round-to-nearest-even, 8-byte stores of the valid rows.
+    if (wt.on) {
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) {
-      if (!row_ok[mt]) continue;
-      const int r = tr.m0 + wm0 + mt * 16 + (lane & 15);
-      uint16_t* drow = tr.d + (size_t)r * p.n + tr.n0 + wn0 + 4 * (lane >> 4);
+      for (int mt = 0; mt < C::MT; ++mt) {
+        if (!wt.row_ok[mt]) continue;
+        const int r = cur.m0 + wm0 + mt * 16 + (lane & 15);
+        uint16_t* drow = cur.d + (size_t)r * p.n + cur.n0 + wn0 + 4 * (lane >> 4);
 #pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt) {
-        const f32x4 v = acc[mt][nt];
-        uint2 packed;
-        packed.x = pack_bf16x2(v[0], v[1]);
-        packed.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(drow + nt * 16) = packed;
+        for (int nt = 0; nt < C::NT; ++nt) {
+          const f32x4 v = wt.acc[mt][nt];
+          uint2 packed;
+          packed.x = pack_bf16x2(v[0], v[1]);
+          packed.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(drow + nt * 16) = packed;
+        }
       }
     }
+    cur = nxt;
+    t = t_next;
   }
-  // The last K steps re-load a block into a stage nobody reads; no wave may
-  // end while such a load can still write its LDS.
+  // The last refill loaded a block nobody reads; no wave may end while such
+  // a load can still write its LDS.
   wait_vmcnt_0();
 }
 
@@ -395,36 +542,39 @@ __global__ void __launch_bounds__(C::THREADS, 1) fp8_gemm_nt_kernel(GemmArgs p) 
 // Launchers
 // ---------------------------------------------------------------------------
 
-using CfgBase = Config<128, 128, 2, 2, 2>;
+using CfgLarge = Config<256, 256, 2, 4, 2>;
 
 template <class C, int KIND>
 static hipError_t launch(const GemmArgs& args, int num_cus, hipStream_t stream) {
-  const size_t lds = 0;  // all LDS is static
   auto kern = fp8_gemm_nt_kernel<C, KIND>;
   int per_cu = 1;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, C::THREADS, lds);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, C::THREADS, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
-  long long slots = (long long)num_cus * per_cu;
-  long long tiles = args.num_tiles;
+  const long long slots = (long long)num_cus * per_cu;
+  const long long tiles = args.num_tiles;
   int grid = (int)(tiles < slots ? tiles : slots);
   if (grid < 1) return hipSuccess;
-  // Keep the grid a multiple of 8 when it is large so the XCD renumbering applies.
+  // Keep a large grid a multiple of 8 so that the XCD renumbering applies.
   if (grid > 8) grid -= grid & 7;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::THREADS), lds, stream, args);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::THREADS), 0, stream, args);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(int kind, GemmArgs args, int num_cus, hipStream_t stream) {
-  using C = CfgBase;
-  args.m_blocks = (kind == KIND_MASKED) ? (args.m + C::BM - 1) / C::BM : (args.m + C::BM - 1) / C::BM;
-  args.n_blocks = args.n / C::BN;
+  using C = CfgLarge;
+  args.m_blocks = (args.m + C::BM - 1) / C::BM;
+  args.n_blocks = (args.n + C::BN - 1) / C::BN;
   if (kind == KIND_MASKED) {
-    args.num_tiles = args.num_groups * args.m_blocks * args.n_blocks;  // upper bound; the kernel recounts
+    // Upper bound for the grid size; the kernel counts the real tiles.
+    args.num_tiles = args.num_groups * args.m_blocks * args.n_blocks;
     return launch<C, KIND_MASKED>(args, num_cus, stream);
   }
+  if (kind == KIND_CONTIGUOUS) {
+    args.num_tiles = C::SLOTS * args.m_blocks * args.n_blocks;
+    return launch<C, KIND_CONTIGUOUS>(args, num_cus, stream);
+  }
   args.num_tiles = args.m_blocks * args.n_blocks;
-  if (kind == KIND_CONTIGUOUS) return launch<C, KIND_CONTIGUOUS>(args, num_cus, stream);
   return launch<C, KIND_DENSE>(args, num_cus, stream);
 }
 
