@@ -306,32 +306,67 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int k, int wave, int lane) {
   return o;
 }
 
-// Loads of K block `kb` of one tile into stage S: the A and B tile rows with
-// the swizzle of lds_offset() (rows past the tile's valid rows read as zero),
-// the tile's LHS scales, and the RHS scale of this wave's columns (returned
-// in a register once the loads have landed).
-template <class C, int S>
-__device__ __forceinline__ float issue_stage(const TileRef& tr, int kb, const GemmArgs& p, int wave, int wn0,
-                                             const LaneOffsets& lo) {
-  static_assert(C::NW * 8 % 16 == 0, "swizzle phase");
-  uint8_t* st = stage_buf<C, S>();
+// Buffer descriptors of K block `kb` of one tile.
+struct StageSrc {
+  __amdgpu_buffer_rsrc_t a, b, sa, sb;
+  uint32_t sb_off;
+};
+
+template <class C>
+__device__ __forceinline__ StageSrc stage_src(const TileRef& tr, int kb, const GemmArgs& p, int wn0) {
+  StageSrc r;
   const uint32_t K = (uint32_t)p.k;
   const int k_blocks = p.k / BK;
   const uint32_t a_rows = (uint32_t)min(max(tr.load_rows - tr.m0, 0), C::BM);
   const uint32_t b_rows = (uint32_t)min(p.n - tr.n0, C::BN);
-  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(tr.a + (size_t)tr.m0 * K + (size_t)kb * BK, a_rows * K);
-  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(tr.b + (size_t)tr.n0 * K + (size_t)kb * BK, b_rows * K);
-  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(tr.sfa + (size_t)kb * p.ld_sfa + tr.m0, a_rows * 4u);
-#pragma unroll
-  for (int j = 0; j < C::A_DMA; ++j) buf_dma16(ra, lo.ab + j * lo.ab_step, st + (j * C::NW + wave) * 1024);
-#pragma unroll
-  for (int j = 0; j < C::B_DMA; ++j)
-    buf_dma16(rb, lo.ab + j * lo.ab_step, st + C::A_BYTES + (j * C::NW + wave) * 1024);
-  buf_dma4(rs, lo.sa, st + C::A_BYTES + C::B_BYTES + wave * 256);
+  r.a = buffer_rsrc(tr.a + (size_t)tr.m0 * K + (size_t)kb * BK, a_rows * K);
+  r.b = buffer_rsrc(tr.b + (size_t)tr.n0 * K + (size_t)kb * BK, b_rows * K);
+  r.sa = buffer_rsrc(tr.sfa + (size_t)kb * p.ld_sfa + tr.m0, a_rows * 4u);
   const float* sfb_row = tr.sfb + (size_t)((min(tr.n0 + wn0, p.n - 1)) / BK) * k_blocks;
-  const uint32_t bits =
-      __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(sfb_row, (uint32_t)k_blocks * 4u), (uint32_t)kb * 4u, 0, 0);
-  return __builtin_bit_cast(float, bits);
+  r.sb = buffer_rsrc(sfb_row, (uint32_t)k_blocks * 4u);
+  r.sb_off = (uint32_t)kb * 4u;
+  return r;
+}
+
+// The loads of one K block into stage S are issued in STAGE_PARTS parts
+// spread over the first bands of the current K step, so that the memory
+// pipeline drains while the matrix cores work: part 0 and 1 the A tile (rows
+// past the tile's valid rows read as zero), part 2 and 3 the B tile (both with
+// the swizzle of lds_offset()), part 3 also the tile's LHS scales and the RHS
+// scale of this wave's columns (returned; usable once the stage has been
+// waited for).
+constexpr int STAGE_PARTS = 4;
+
+template <class C, int S, int PART>
+__device__ __forceinline__ float issue_part(const StageSrc& r, int wave, const LaneOffsets& lo) {
+  static_assert(C::A_DMA % 2 == 0 && C::B_DMA % 2 == 0, "loads split in halves");
+  uint8_t* st = stage_buf<C, S>();
+  if constexpr (PART < 2) {
+#pragma unroll
+    for (int j = PART * C::A_DMA / 2; j < (PART + 1) * C::A_DMA / 2; ++j)
+      buf_dma16(r.a, lo.ab + j * lo.ab_step, st + (j * C::NW + wave) * 1024);
+    return 0.f;
+  } else {
+#pragma unroll
+    for (int j = (PART - 2) * C::B_DMA / 2; j < (PART - 1) * C::B_DMA / 2; ++j)
+      buf_dma16(r.b, lo.ab + j * lo.ab_step, st + C::A_BYTES + (j * C::NW + wave) * 1024);
+    if constexpr (PART == 3) {
+      buf_dma4(r.sa, lo.sa, st + C::A_BYTES + C::B_BYTES + wave * 256);
+      const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(r.sb, r.sb_off, 0, 0);
+      return __builtin_bit_cast(float, bits);
+    }
+    return 0.f;
+  }
+}
+
+template <class C, int S>
+__device__ __forceinline__ float issue_stage(const TileRef& tr, int kb, const GemmArgs& p, int wave, int wn0,
+                                             const LaneOffsets& lo) {
+  const StageSrc r = stage_src<C>(tr, kb, p, wn0);
+  issue_part<C, S, 0>(r, wave, lo);
+  issue_part<C, S, 1>(r, wave, lo);
+  issue_part<C, S, 2>(r, wave, lo);
+  return issue_part<C, S, 3>(r, wave, lo);
 }
 
 // Wait until this wave's loads of the stage about to be read have landed,
@@ -379,22 +414,25 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const TileRef& cur, 
       wait_stage<C>(C::STAGES - 2);
       wait_lgkmcnt_0();
       barrier();
-      float sb;
       // Refill the stage every wave finished reading in the previous step.
       // Past the end of this tile the loads belong to the next one; with no
       // next tile the last block is loaded again (nobody reads it): the
       // loads are issued unconditionally, since a branch here would make the
       // compiler wait for them before reading the current stage.
-      {
-        const int ahead = kb + C::STAGES - 1;
-        const bool own = ahead < k_blocks;
-        const TileRef& src = (own || !nxt.active) ? cur : nxt;
-        const int kb_load = own ? ahead : (nxt.active ? ahead - k_blocks : k_blocks - 1);
-        const float sb_loaded = issue_stage<C, (s + C::STAGES - 1) % C::STAGES>(src, kb_load, p, wave, wn0, lo);
-        sb = sb_next;          // this step's RHS scale, loaded with its stage
-        sb_next = sb_loaded;
+      constexpr int sr = (s + C::STAGES - 1) % C::STAGES;
+      const int ahead = kb + C::STAGES - 1;
+      const bool own = ahead < k_blocks;
+      const TileRef& src = (own || !nxt.active) ? cur : nxt;
+      const int kb_load = own ? ahead : (nxt.active ? ahead - k_blocks : k_blocks - 1);
+      const StageSrc rsrc = stage_src<C>(src, kb_load, p, wn0);
+      const float sb = sb_next;  // this step's RHS scale, loaded with its stage
+      if (!wt.on) {
+        issue_part<C, sr, 0>(rsrc, wave, lo);
+        issue_part<C, sr, 1>(rsrc, wave, lo);
+        issue_part<C, sr, 2>(rsrc, wave, lo);
+        sb_next = issue_part<C, sr, 3>(rsrc, wave, lo);
+        return;
       }
-      if (!wt.on) return;
 
       const uint8_t* As = stage_buf<C, s>();
       const uint8_t* Bs = As + C::A_BYTES;
@@ -403,7 +441,8 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const TileRef& cur, 
       // Pipeline over the wave's 16-row bands: the next band's A fragment and
       // scale are read while this band's MFMAs run; each band's partial sums
       // are promoted right after its MFMAs (the other wave on the SIMD keeps
-      // the matrix core busy meanwhile).
+      // the matrix core busy meanwhile); the first bands also issue the
+      // refill loads.
       i32x8 bf[C::NT];
 #pragma unroll
       for (int nt = 0; nt < C::NT; ++nt) bf[nt] = read_frag(Bs, wn0 + nt * 16 + (lane & 15), lane);
@@ -417,6 +456,10 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const TileRef& cur, 
           af_next = read_frag(As, wm0 + (mt + 1) * 16 + (lane & 15), lane);
           sa_next = SAs[sa_index<C>(wm0 + (mt + 1) * 16 + (lane & 15))];
         }
+        if (mt == 0) issue_part<C, sr, 0>(rsrc, wave, lo);
+        if (mt == 1) issue_part<C, sr, 1>(rsrc, wave, lo);
+        if (mt == 2) issue_part<C, sr, 2>(rsrc, wave, lo);
+        if (mt == 3) sb_next = issue_part<C, sr, 3>(rsrc, wave, lo);
         f32x4 part[C::NT];
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt)
@@ -429,9 +472,10 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const TileRef& cur, 
           af = af_next;
           sa = sa_next;
         }
-        // Issue order: the next band's reads first, then the MFMAs, then the
-        // promotion of this band.
+        // Issue order: the next band's reads and this band's share of the
+        // refill first, then the MFMAs, then the promotion of this band.
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS reads
+        if (mt < STAGE_PARTS) __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);  // VMEM loads
         __builtin_amdgcn_sched_group_barrier(0x008, C::NT, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 4 * C::NT + 1, 0);  // VALU
         __builtin_amdgcn_sched_barrier(0);
