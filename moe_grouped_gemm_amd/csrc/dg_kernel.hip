@@ -282,13 +282,35 @@ __device__ __forceinline__ TileRef resolve_tile(const GemmArgs& p, int t, int nu
   return tr;
 }
 
+__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // The first active tile at or after t in this CTA's sequence t, t+grid, ...
+// Every field is the same in all lanes; it is moved to scalar registers.
 template <class C, int KIND>
 __device__ __forceinline__ TileRef next_active(const GemmArgs& p, int& t, int grid, int num_tiles,
                                                const int* s_prefix) {
   for (; t < num_tiles; t += grid) {
     TileRef tr = resolve_tile<C, KIND>(p, t, num_tiles, s_prefix);
-    if (tr.active) return tr;
+    if (tr.active) {
+      tr.a = uniform_ptr(tr.a);
+      tr.sfa = uniform_ptr(tr.sfa);
+      tr.b = uniform_ptr(tr.b);
+      tr.sfb = uniform_ptr(tr.sfb);
+      tr.d = uniform_ptr(tr.d);
+      tr.group = uniform_int(tr.group);
+      tr.m0 = uniform_int(tr.m0);
+      tr.n0 = uniform_int(tr.n0);
+      tr.load_rows = uniform_int(tr.load_rows);
+      tr.valid_rows = uniform_int(tr.valid_rows);
+      return tr;
+    }
   }
   TileRef none;
   none.active = false;
