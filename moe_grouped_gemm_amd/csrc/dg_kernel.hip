@@ -39,6 +39,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) i32x4 global_i32x4;
 
 constexpr int BK = 128;        // K block = scale granularity
 constexpr int ROW_BYTES = 128; // one tile row of one K block
@@ -576,7 +577,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& cur
       const uint4 q = *reinterpret_cast<const uint4*>(scr + slot_off(row, sl));
       if ((valid >> row) & 1) {
         uint16_t* drow = cur.d + (size_t)(cur.m0 + wm0 + mt * 16 + row) * p.n + cur.n0 + wn0 + 8 * sl;
-        *reinterpret_cast<uint4*>(drow) = q;
+        // A global (not flat) store, which the LDS counter does not track, and
+        // non-temporal: the output is not read again by this kernel.
+        __builtin_nontemporal_store((i32x4){(int)q.x, (int)q.y, (int)q.z, (int)q.w},
+                                    (global_i32x4*)drow);
       }
     }
   }
