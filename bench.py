@@ -36,8 +36,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 def parse_args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    # Enough untimed launches (about 0.1 s of GPU work on the headline
+    # workload) for the clocks to settle before timing.
+    p.add_argument("--warmup", type=int, default=1000)
     p.add_argument("--only", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true")
@@ -197,8 +199,8 @@ def main():
             s = synth.workload_spec(idx)
             wx = synth.make_workload(s, seed=0, device=dev)
             torch.cuda.synchronize()
-            steps = max(5, args.steps // 2)
-            ms, kms = time_workload(wx, steps, max(2, args.warmup // 2))
+            steps = max(5, args.steps // 4)
+            ms, kms = time_workload(wx, steps, max(2, args.warmup // 10))
             tf = wx.flops() / (kms * 1e-3) / 1e12
             gbs = wx.algorithmic_bytes() / (kms * 1e-3) / 1e9
             extra[s.name] = {"kernel_ms": round(kms, 5), "tflops": round(tf, 2),
