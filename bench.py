@@ -29,7 +29,9 @@ METRIC = "TFLOPS & % FP8 MFMA peak: dense, m-grouped contiguous, masked FP8 NT G
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 HEADLINE = 1                 # dense 4096x7168x2048
-KERNEL_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_amd", "csrc", "dg_kernel.hip")
+# The device code of the kernels (the traffic figures are valid for it only).
+KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_gemm_amd", "csrc", f)
+                  for f in ("dg_device.h", "dg_kernel.hip", "dg_kernel_deep.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -48,8 +50,11 @@ def parse_args():
 
 
 def kernel_source_sha() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload_name: str):

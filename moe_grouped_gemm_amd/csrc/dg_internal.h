@@ -30,4 +30,13 @@ struct GemmArgs {
 // Enqueues the kernel for `kind` on `stream`; arguments already validated.
 hipError_t launch_gemm(int kind, GemmArgs args, int num_cus, hipStream_t stream);
 
+// K blocks from which launch_gemm() uses the pipeline of dg_kernel_deep.hip,
+// which loads operands further ahead (measured on MI355X: 4-4.5% faster on
+// the K = 7168 grouped workloads, 2-3% slower at K = 2048).
+constexpr int DEEP_MIN_K_BLOCKS = 32;
+
+namespace deep {
+hipError_t launch_gemm(int kind, GemmArgs args, int num_cus, hipStream_t stream);
+}
+
 }  // namespace dg

@@ -46,6 +46,11 @@ DENSE_SHAPES = [
     (64, 256, 4096),
     (1000, 640, 384),
     (2048, 1024, 1024),  # more tiles than CUs
+    (300, 896, 1024),    # N = 3.5 tiles
+    (1, 896, 128),
+    # K of 32 blocks and more: the deep-prefetch pipeline
+    (300, 384, 4096),
+    (257, 1792, 8192),
 ]
 
 
@@ -82,7 +87,7 @@ def _dev_fp8(x, dev):
     return torch.from_numpy(x).to(dev).view(torch.float8_e4m3fn)
 
 
-@pytest.mark.parametrize("m,n,k", [(200, 256, 1024), (129, 384, 2048)])
+@pytest.mark.parametrize("m,n,k", [(200, 256, 1024), (129, 384, 2048), (77, 896, 512), (65, 256, 4096)])
 def test_dense_integer_exact_bitwise(dev, m, n, k):
     _say(f"dense integer-exact {m}x{n}x{k}")
     a, sfa, b, sfb = _int_exact(m, n, k, seed=m)
@@ -130,6 +135,8 @@ def _check_contiguous(w, d, what):
     ([130, 0, 77, 256, 1], 256, 512),
     ([128], 128, 128),
     ([5, 300, 1, 129], 384, 1024),
+    ([130, 0, 77, 256, 1], 896, 512),
+    ([130, 0, 77, 256, 1], 256, 4096),
 ])
 def test_contiguous_small(dev, rows, n, k):
     _say(f"contiguous rows={rows} n={n} k={k}")
@@ -199,6 +206,8 @@ def _check_masked(w, d, counts, what):
     ([0, 1, 200, 77], 200, 256, 512),
     ([256, 129], 256, 384, 1024),
     ([3], 64, 128, 128),
+    ([0, 1, 200, 77], 200, 896, 512),
+    ([0, 1, 200, 77], 200, 256, 4096),
 ])
 def test_masked_small(dev, counts, max_m, n, k):
     _say(f"masked counts={counts} max_m={max_m} n={n} k={k}")
