@@ -93,6 +93,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
+// The LDS destination of a direct-to-LDS load, given as a bare LDS byte
+// address: the compiler then does not associate the load with an LDS variable
+// and adds no waits of its own before later LDS accesses (it cannot tell
+// which parts of a variable a load in flight writes, and would wait for every
+// load in flight before reading or writing any of it). Every access to loaded
+// data is ordered after its load explicitly: a vmcnt wait, then a barrier.
+__device__ __forceinline__ lds_void* lds_dest(uint32_t lds_addr) {
+  return (lds_void*)(uintptr_t)__builtin_amdgcn_readfirstlane(lds_addr);
+}
+
 // Maps a linear tile index to (m block, n block), walking panels of
 // `panel_m` consecutive M blocks across all N blocks so that tiles issued
 // together share A and B panels in L2.

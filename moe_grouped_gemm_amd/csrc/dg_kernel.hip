@@ -27,9 +27,7 @@
 
 namespace dg {
 
-// One LDS buffer per pipeline stage, each its own variable: the compiler can
-// then tell a direct-to-LDS load into one stage from reads of another and
-// does not wait for the in-flight stage before reading the current one.
+// One LDS buffer per pipeline stage.
 template <class C, int S>
 __device__ __forceinline__ uint8_t* stage_buf() {
   static_assert(S < C::STAGES, "stage index");
@@ -37,13 +35,20 @@ __device__ __forceinline__ uint8_t* stage_buf() {
   return buf;
 }
 
-// One wave-wide 16-byte buffer load per lane into LDS: lane l writes
-// lds_base + 16 * l (lds_base is the same for the whole wave).
-__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, 0, 0, 0);
+// LDS byte address of stage S (the variable's own address, cast once).
+template <class C, int S>
+__device__ __forceinline__ uint32_t stage_addr() {
+  return (uint32_t)(uintptr_t)(lds_void*)stage_buf<C, S>();
 }
-__device__ __forceinline__ void buf_dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 4, voff, 0, 0, 0);
+
+// One wave-wide 16-byte buffer load per lane into LDS: lane l writes LDS byte
+// address lds_base + 16 * l (lds_base is the same for the whole wave).
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_dest(lds_base), 16, voff, 0, 0, 0);
+}
+// The same with 4 bytes per lane: lane l writes lds_base + 4 * l.
+__device__ __forceinline__ void buf_dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_dest(lds_base), 4, voff, 0, 0, 0);
 }
 
 // Per-lane byte offsets of this lane's loads within a tile, fixed for the
@@ -146,7 +151,7 @@ constexpr int STAGE_PARTS = 4;
 template <class C, int S, int PART>
 __device__ __forceinline__ float issue_part(const StageSrc& r, int wave, const LaneOffsets& lo) {
   static_assert(C::A_DMA % 2 == 0 && C::B_DMA % 2 == 0, "loads split in halves");
-  uint8_t* st = stage_buf<C, S>();
+  const uint32_t st = stage_addr<C, S>();
   if constexpr (PART < 2) {
 #pragma unroll
     for (int j = PART * C::A_DMA / 2; j < (PART + 1) * C::A_DMA / 2; ++j)
@@ -254,11 +259,18 @@ __device__ __forceinline__ float sa_at(uint32_t off, int mt) {
 // the stage the tile's last step read; no wave reads that stage again before
 // the next barrier, and only this wave's own refill loads, issued later,
 // overwrite these slots. 16-byte slots are XOR-swizzled by row.
+//
+// Each staging access is a vector load or store at one offset from the stage
+// buffer's own address: the compiler then knows which LDS variable it
+// touches (a struct-typed or longer pointer chain loses that, and it would
+// wait for every load in flight before each access).
 template <class C, int KIND, int S>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& cur, const RowMask& cm,
                                            const WaveTile<C>& wt, int wave, int wm0, int wn0, int lane) {
   static_assert(C::WN * 2 == 128 && C::B_DMA >= 2, "one 128-byte row segment per wave and band");
-  uint8_t* scr = stage_buf<C, S>() + C::A_BYTES + wave * 1024;  // slot j of the wave at + j * NW * 1024
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  uint8_t* const st = stage_buf<C, S>();
+  const int wbase = C::A_BYTES + wave * 1024;  // slot j of the wave at + j * NW * 1024
   const int r = lane & 15, g = lane >> 4;
   auto slot_off = [](int row, int sl) { return (row >> 3) * C::NW * 1024 + (row & 7) * 128 + ((sl ^ (row & 7)) << 4); };
 #pragma unroll
@@ -268,23 +280,20 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& cur
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
       const f32x4 v = wt.acc[mt][nt];
-      uint2 packed;
-      packed.x = pack_bf16x2(v[0], v[1]);
-      packed.y = pack_bf16x2(v[2], v[3]);
+      const i32x2 packed = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
       // columns 16 nt + 4 g .. + 3: half (g & 1) of 16-byte slot 2 nt + g / 2
-      *reinterpret_cast<uint2*>(scr + slot_off(r, 2 * nt + (g >> 1)) + (g & 1) * 8) = packed;
+      *reinterpret_cast<i32x2*>(st + (wbase + slot_off(r, 2 * nt + (g >> 1)) + (g & 1) * 8)) = packed;
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int row = (lane >> 3) + 8 * half;
       const int sl = lane & 7;
-      const uint4 q = *reinterpret_cast<const uint4*>(scr + slot_off(row, sl));
+      const i32x4 q = *reinterpret_cast<const i32x4*>(st + (wbase + slot_off(row, sl)));
       if ((valid >> row) & 1) {
         uint16_t* drow = cur.d + (size_t)(cur.m0 + wm0 + mt * 16 + row) * p.n + cur.n0 + wn0 + 8 * sl;
         // A global (not flat) store, which the LDS counter does not track, and
         // non-temporal: the output is not read again by this kernel.
-        __builtin_nontemporal_store((i32x4){(int)q.x, (int)q.y, (int)q.z, (int)q.w},
-                                    (global_i32x4*)drow);
+        __builtin_nontemporal_store(q, (global_i32x4*)drow);
       }
     }
   }

@@ -21,14 +21,6 @@ namespace deep {
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-// The LDS destination of a direct-to-LDS load, as a bare LDS address: the
-// compiler then does not associate the load with an LDS variable and adds
-// no waits of its own before reads of LDS. Every read of loaded data is
-// ordered after its load explicitly (a vmcnt wait, then a barrier).
-__device__ __forceinline__ lds_void* lds_dest(uint32_t lds_addr) {
-  return (lds_void*)(uintptr_t)__builtin_amdgcn_readfirstlane(lds_addr);
-}
-
 // One wave-wide 16-byte buffer load per lane into LDS from byte offset
 // voff + soff (soff wave-uniform, in a scalar register): lane l writes LDS
 // byte address lds_base + 16 * l (lds_base is the same for the whole wave).
