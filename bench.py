@@ -2,13 +2,13 @@
 
 One step = one call of the GEMM on one batch of synthetic input already in
 HBM. The headline workload is the dense 4096x7168x2048 GEMM; the grouped
-contiguous, masked-decode and small dense workloads are measured after it
-and reported under "workloads". Prints ONE JSON line.
+contiguous, masked-decode, no-padding and small dense workloads are measured
+after it and reported under "workloads". Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only INDEX]
                     [--no-cpu-baseline] [--no-extra] [--copy-calibration]
 
---only INDEX times a single workload (0..4), for profiling runs.
+--only INDEX times a single workload (0..5), for profiling runs.
 --copy-calibration runs a plain 1 GiB device copy (for scaling HBM traffic
 counters) and exits.
 """
@@ -200,7 +200,7 @@ def main():
 
     if args.only is None and not args.no_extra:
         extra = {}
-        for idx in (0, 2, 3, 4):
+        for idx in (i for i in range(synth.NUM_WORKLOADS) if i != HEADLINE):
             s = synth.workload_spec(idx)
             wx = synth.make_workload(s, seed=0, device=dev)
             torch.cuda.synchronize()

@@ -41,7 +41,7 @@
  * the only library state is the CU-count setting.
  *
  * Limits: K <= 2^20, N <= 2^20, every operand < 2^40 bytes, num_groups <= 4096
- * for the masked layout.
+ * for the masked layout and <= 2048 for the no-padding layout.
  */
 #ifndef DG_H
 #define DG_H
@@ -115,6 +115,30 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa,
                                           void* d, const int32_t* masked_m,
                                           int num_groups, int max_m, int n, int k,
                                           void* stream);
+
+/*
+ * M-grouped FP8 NT GEMM, no-padding layout ("DeepGEMM for PPU" README,
+ * "Grouped GEMMs (nopad layout)"): the groups' rows are concatenated with no
+ * alignment padding, and a per-group row count replaces the per-row index.
+ *   a   [m][k] E4M3: group 0's rows, then group 1's, ... (any counts)
+ *   sfa [k/128][dg_get_tma_aligned_size(m,4)] float32
+ *   b   [num_groups][n][k] E4M3          sfb [num_groups][n/128][k/128] float32
+ *   d   [m][n] BF16
+ *   group_rows [num_groups] int32 (device): rows of each group, read by the
+ *       kernel only. A negative count counts as zero.
+ * Group g owns rows [s_g, e_g) with s_g = min(sum_{j<g} c_j, m) and
+ * e_g = min(s_g + c_g, m), c_j = max(group_rows[j], 0): rows at or past m
+ * do not exist, so a group that would reach past them is cut off there.
+ * Those rows of d are written; rows at or past min(sum_j c_j, m) are
+ * untouched. As for the masked layout the launch shape does not depend on
+ * the counts, so one captured graph serves any group_rows contents.
+ * m >= 0 (any value).
+ */
+dg_status dg_m_grouped_fp8_gemm_nt_nopad(const void* a, const float* sfa,
+                                         const void* b, const float* sfb,
+                                         void* d, const int32_t* group_rows,
+                                         int m, int n, int k, int num_groups,
+                                         void* stream);
 
 /* Row alignment of each group's segment in the contiguous layout: 128
  * ("DeepGEMM Compatibility Wrapper" page, "Contiguous Grouped GEMM

@@ -37,6 +37,7 @@ int effective_cus() {
 constexpr long long kMaxDim = 1 << 20;
 constexpr long long kMaxBytes = 1LL << 40;
 constexpr int kMaxMaskedGroups = dg::MAX_MASKED_GROUPS;
+constexpr int kMaxNopadGroups = dg::MAX_NOPAD_GROUPS;
 
 dg_status common_checks(const void* a, const float* sfa, const void* b, const float* sfb, const void* d,
                         long long n, long long k) {
@@ -129,6 +130,32 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, const
   args.num_groups = num_groups;
   args.ld_sfa = tma_aligned(max_m, 4);
   return launch(dg::KIND_MASKED, args, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_nopad(const void* a, const float* sfa, const void* b, const float* sfb, void* d,
+                                         const int32_t* group_rows, int m, int n, int k, int num_groups,
+                                         void* stream) {
+  if (dg_status s = common_checks(a, sfa, b, sfb, d, n, k)) return s;
+  if (!group_rows) return DG_ERR_NULL;
+  if (m < 0 || num_groups < 0) return DG_ERR_SHAPE;
+  if (num_groups > kMaxNopadGroups) return DG_ERR_UNSUPPORTED;
+  if ((long long)m * k >= kMaxBytes || (long long)m * n * 2 >= kMaxBytes ||
+      (long long)num_groups * n * k >= kMaxBytes)
+    return DG_ERR_UNSUPPORTED;
+  if (m == 0 || num_groups == 0) return DG_OK;
+  dg::GemmArgs args{};
+  args.a = static_cast<const uint8_t*>(a);
+  args.sfa = sfa;
+  args.b = static_cast<const uint8_t*>(b);
+  args.sfb = sfb;
+  args.d = static_cast<uint16_t*>(d);
+  args.aux = group_rows;
+  args.m = m;
+  args.n = n;
+  args.k = k;
+  args.num_groups = num_groups;
+  args.ld_sfa = tma_aligned(m, 4);
+  return launch(dg::KIND_NOPAD, args, stream);
 }
 
 int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }

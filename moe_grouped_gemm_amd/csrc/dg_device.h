@@ -127,14 +127,70 @@ __device__ __forceinline__ int aux_scalar(const int* aux, int i) {
   return base[__builtin_amdgcn_readfirstlane(i)];
 }
 
+// The group table of the layouts whose row counts are read on the device
+// (masked, no-padding), built by wave 0 at kernel start from the counts in
+// aux, 64 groups at a time with an in-wave scan:
+//   tab[g], g = 0..G:          tiles of the groups before g (each group: its
+//                              BM-row blocks times the N blocks);
+//   tab[G + 1 + g], g = 0..G:  no-padding only: first row of group g. The
+//                              groups' rows follow one another from row 0;
+//                              whatever lies at or past row m is cut off.
+// A count is clamped to [0, m] (masked: m is max_m). Returns the table once
+// every wave of the workgroup can read it.
+template <class C, int KIND>
+__device__ int* group_table(const GemmArgs& p, int tid) {
+  static_assert(counts_on_device(KIND), "masked and no-padding layouts only");
+  __shared__ int tab[GROUP_TABLE_INTS];
+  const int G = p.num_groups;
+  if (tid < 64) {
+    const int lane = tid;
+    int tiles_before = 0;
+    long long rows_before = 0;
+    for (int g0 = 0; g0 < G; g0 += 64) {
+      const int g = g0 + lane;
+      const int rows = g < G ? min(max(p.aux[g], 0), p.m) : 0;
+      long long rows_incl = rows;
+      for (int d = 1; d < 64; d <<= 1) {
+        const long long v = __shfl_up(rows_incl, d);
+        if (lane >= d) rows_incl += v;
+      }
+      int first = 0, count = rows;
+      if constexpr (KIND == KIND_NOPAD) {
+        const long long s = rows_before + rows_incl - rows;
+        first = (int)min(s, (long long)p.m);
+        count = (int)min(s + rows, (long long)p.m) - first;
+      }
+      const int tiles = (count + C::BM - 1) / C::BM * p.n_blocks;
+      int tiles_incl = tiles;
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(tiles_incl, d);
+        if (lane >= d) tiles_incl += v;
+      }
+      if (g < G) {
+        tab[g] = tiles_before + tiles_incl - tiles;
+        if constexpr (KIND == KIND_NOPAD) tab[G + 1 + g] = first;
+      }
+      tiles_before += __shfl(tiles_incl, 63);
+      rows_before += __shfl(rows_incl, 63);
+    }
+    if (lane == 0) {
+      tab[G] = tiles_before;
+      if constexpr (KIND == KIND_NOPAD) tab[2 * G + 1] = (int)min(rows_before, (long long)p.m);
+    }
+  }
+  __syncthreads();
+  return tab;
+}
+
 // Resolves linear tile index t of layout KIND. Tile order:
 //   dense:      raster over (M block, N block);
 //   contiguous: slot-major, then raster over (BM-row block, N block); slot j
 //               of a block is the j-th distinct valid group among its 128-row
 //               segment blocks (a block holds two groups only where a group's
 //               segment ends inside it), so slot 0 carries nearly all work;
-//   masked:     per group (prefix sums of the per-group tile counts, read
-//               from masked_m on the device), then N block, then M block.
+//   masked,
+//   no-padding: per group (the group table, built on the device from the
+//               per-group row counts), then N block, then M block.
 template <class C, int KIND>
 __device__ __forceinline__ TileRef resolve_tile(const GemmArgs& p, int t, int num_tiles, const int* s_prefix) {
   TileRef tr;
@@ -142,27 +198,38 @@ __device__ __forceinline__ TileRef resolve_tile(const GemmArgs& p, int t, int nu
   if (t >= num_tiles) return tr;
   const size_t K = (size_t)p.k;
   const int k_blocks = p.k / BK;
-  if constexpr (KIND == KIND_MASKED) {
+  if constexpr (counts_on_device(KIND)) {
     int lo = 0, hi = p.num_groups - 1;  // last g with prefix[g] <= t: a group with tiles
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_prefix[mid] <= t) lo = mid; else hi = mid - 1;
     }
     const int g = lo;
-    const int v = min(max(aux_scalar(p.aux, g), 0), p.m);
+    int v;
+    if constexpr (KIND == KIND_NOPAD) {
+      // The group's rows: a row range of the shared A, sfa and D.
+      const int first = s_prefix[p.num_groups + 1 + g];
+      v = s_prefix[p.num_groups + 2 + g] - first;
+      tr.a = p.a + (size_t)first * K;
+      tr.sfa = p.sfa + first;
+      tr.d = p.d + (size_t)first * p.n;
+    } else {
+      // The group's own [max_m] slice of A, sfa and D.
+      v = min(max(aux_scalar(p.aux, g), 0), p.m);
+      tr.a = p.a + (size_t)g * p.m * K;
+      tr.sfa = p.sfa + (size_t)g * k_blocks * p.ld_sfa;
+      tr.d = p.d + (size_t)g * p.m * p.n;
+    }
     const int mblocks = (v + C::BM - 1) / C::BM;
     const int local = t - s_prefix[g];
     const int nb = local / mblocks;
     const int mb = local - nb * mblocks;
     tr.group = g;
-    tr.a = p.a + (size_t)g * p.m * K;
-    tr.sfa = p.sfa + (size_t)g * k_blocks * p.ld_sfa;
     tr.b = p.b + (size_t)g * p.n * K;
     tr.sfb = p.sfb + (size_t)g * (p.n / BK) * k_blocks;
-    tr.d = p.d + (size_t)g * p.m * p.n;
     tr.m0 = mb * C::BM;
     tr.n0 = nb * C::BN;
-    tr.load_rows = v;        // rows past masked_m are never fetched
+    tr.load_rows = v;        // rows past the group's count are never fetched
     tr.valid_rows = v;
     tr.active = true;
   } else {

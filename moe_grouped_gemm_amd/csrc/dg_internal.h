@@ -7,10 +7,17 @@
 
 namespace dg {
 
-enum { KIND_DENSE = 0, KIND_CONTIGUOUS = 1, KIND_MASKED = 2 };
+enum { KIND_DENSE = 0, KIND_CONTIGUOUS = 1, KIND_MASKED = 2, KIND_NOPAD = 3 };
 
-// Largest group count of the masked layout (the per-group tile prefix lives in LDS).
-constexpr int MAX_MASKED_GROUPS = 4096;
+// Layouts whose tiles the kernel finds from per-group row counts read on the
+// device (a group table in LDS, see group_table()).
+constexpr bool counts_on_device(int kind) { return kind == KIND_MASKED || kind == KIND_NOPAD; }
+
+// Size of the group table in LDS: the masked layout keeps G + 1 tile
+// prefixes, the no-padding layout G + 1 tile prefixes and G + 1 row offsets.
+constexpr int GROUP_TABLE_INTS = 4098;
+constexpr int MAX_MASKED_GROUPS = GROUP_TABLE_INTS - 2;
+constexpr int MAX_NOPAD_GROUPS = GROUP_TABLE_INTS / 2 - 1;
 
 // Kernel arguments, passed by value. Byte pointers: A and B are E4M3 codes,
 // D is BF16 bits.
@@ -20,8 +27,9 @@ struct GemmArgs {
   const uint8_t* b;
   const float* sfb;
   uint16_t* d;
-  const int32_t* aux;  // contiguous: grouped_layout[m]; masked: masked_m[G]; dense: unused
-  int m;               // dense/contiguous: rows of A and D; masked: max_m
+  const int32_t* aux;  // contiguous: grouped_layout[m]; masked: masked_m[G]; no-padding: rows of
+                       // each group [G]; dense: unused
+  int m;               // dense/contiguous/no-padding: rows of A and D; masked: max_m
   int n, k, num_groups;
   int ld_sfa;          // leading dimension of the transposed LHS scales
   int m_blocks, n_blocks, num_tiles;  // filled in by launch_gemm

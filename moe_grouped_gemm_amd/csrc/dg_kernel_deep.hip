@@ -280,11 +280,11 @@ __device__ __forceinline__ float sb_at(int wave) {
   return *reinterpret_cast<const float*>(region<C, S, 0>() + C::X_SB_OFF + (wave % C::WAVES_N) * C::WN / 128 * 256);
 }
 
-// Rows per pass of the epilogue. The masked layout keeps its per-group tile
-// prefix in LDS too and stages half bands.
+// Rows per pass of the epilogue. The masked and no-padding layouts keep
+// their group table in LDS too and stage half bands.
 template <int KIND>
 constexpr int epilogue_rows() {
-  return KIND == KIND_MASKED ? 8 : 16;
+  return counts_on_device(KIND) ? 8 : 16;
 }
 
 // Writes one finished tile of a wave as BF16 (round to nearest even). Each
@@ -540,22 +540,11 @@ __global__ void __launch_bounds__(C::THREADS, 1) fp8_gemm_nt_kernel(GemmArgs p) 
   const int wn0 = wave_n * C::WN;
   const int k_blocks = p.k / BK;
 
-  // Per-group tile counts for the masked layout, read on the device.
+  // The masked and no-padding layouts count their tiles on the device.
   int num_tiles = p.num_tiles;
   [[maybe_unused]] int* s_prefix = nullptr;
-  if constexpr (KIND == KIND_MASKED) {
-    __shared__ int prefix[MAX_MASKED_GROUPS + 1];
-    s_prefix = prefix;
-    if (tid == 0) {
-      int acc = 0;
-      for (int g = 0; g < p.num_groups; ++g) {
-        s_prefix[g] = acc;
-        const int v = min(max(p.aux[g], 0), p.m);
-        acc += (v + C::BM - 1) / C::BM * p.n_blocks;
-      }
-      s_prefix[p.num_groups] = acc;
-    }
-    __syncthreads();
+  if constexpr (counts_on_device(KIND)) {
+    s_prefix = group_table<C, KIND>(p, tid);
     num_tiles = s_prefix[p.num_groups];
   }
 
@@ -680,6 +669,11 @@ hipError_t launch_gemm(int kind, GemmArgs args, int num_cus, hipStream_t stream)
     // Upper bound for the grid size; the kernel counts the real tiles.
     args.num_tiles = args.num_groups * args.m_blocks * args.n_blocks;
     return launch<C, KIND_MASKED>(args, num_cus, stream);
+  }
+  if (kind == KIND_NOPAD) {
+    // Upper bound: each group adds at most one partial row block.
+    args.num_tiles = (args.m_blocks + args.num_groups) * args.n_blocks;
+    return launch<C, KIND_NOPAD>(args, num_cus, stream);
   }
   if (kind == KIND_CONTIGUOUS) {
     args.num_tiles = C::SLOTS * args.m_blocks * args.n_blocks;

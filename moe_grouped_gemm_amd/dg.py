@@ -27,6 +27,7 @@ SIGNATURES = [
     ("dg_fp8_gemm_nt", [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp], _i),
     ("dg_m_grouped_fp8_gemm_nt_contiguous", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     ("dg_m_grouped_fp8_gemm_nt_masked", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
+    ("dg_m_grouped_fp8_gemm_nt_nopad", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     ("dg_get_mk_alignment_for_contiguous_layout", [], _i),
     ("dg_get_tma_aligned_size", [_i, _i], _i),
     ("dg_get_num_cus", [], _i),
@@ -116,7 +117,7 @@ def get_mn_major_tma_aligned_tensor(sf: torch.Tensor) -> torch.Tensor:
 
 
 # ---------------------------------------------------------------------------
-# The three GEMMs
+# The GEMMs
 # ---------------------------------------------------------------------------
 
 def fp8_gemm_nt(a, sfa, b, sfb, d) -> torch.Tensor:
@@ -190,8 +191,33 @@ def m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, d, masked_m) -> torch.Tensor:
     return d
 
 
+def m_grouped_fp8_gemm_nt_nopad(a, sfa, b, sfb, d, group_rows) -> torch.Tensor:
+    """No-padding grouped GEMM; group_rows [G] int32 (device) holds each
+    group's row count, the groups' rows following one another from row 0 of
+    a with no alignment padding. a [M, K], sfa [K/128, tma_aligned(M)],
+    b [G, N, K], sfb [G, N/128, K/128], d [M, N]."""
+    dev = a.device
+    m, k = a.shape
+    g, n, _ = b.shape
+    _need(a, "a", torch.float8_e4m3fn, 2, dev)
+    _need(b, "b", torch.float8_e4m3fn, 3, dev)
+    _need(sfa, "sfa", torch.float32, 2, dev)
+    _need(sfb, "sfb", torch.float32, 3, dev)
+    _need(d, "d", torch.bfloat16, 2, dev)
+    _need(group_rows, "group_rows", torch.int32, 1, dev)
+    if b.shape[2] != k or tuple(d.shape) != (m, n) or group_rows.shape[0] != g:
+        raise ValueError("shape mismatch between a, b, d and group_rows")
+    if tuple(sfa.shape) != (k // 128, get_tma_aligned_size(m, 4)) or tuple(sfb.shape) != (g, n // 128, k // 128):
+        raise ValueError("scale shapes do not match the (1, 128, 128) recipe layout")
+    _check(lib().dg_m_grouped_fp8_gemm_nt_nopad(
+        a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(), d.data_ptr(), group_rows.data_ptr(),
+        m, n, k, g, _stream(a)), "dg_m_grouped_fp8_gemm_nt_nopad")
+    return d
+
+
 def run_workload(w, d: torch.Tensor) -> torch.Tensor:
-    """Runs the GEMM that matches a synth workload (Dense / Contiguous / Masked)."""
+    """Runs the GEMM that matches a synth workload (Dense / Contiguous /
+    Masked / Nopad)."""
     kind = type(w).__name__
     if kind == "Dense":
         return fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d)
@@ -199,4 +225,6 @@ def run_workload(w, d: torch.Tensor) -> torch.Tensor:
         return m_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout)
     if kind == "Masked":
         return m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m)
+    if kind == "Nopad":
+        return m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows)
     raise TypeError(kind)

@@ -3,7 +3,8 @@
 This module only makes inputs: N(0,1) float32 operands quantised to OCP E4M3
 with one float32 scale per 1x128 LHS block and per 128x128 RHS block
 (scale = max(amax, 1e-4) / 448), the M-major aligned LHS-scale layout, the
-contiguous-layout row->group index and the masked-layout valid-row counts. It
+contiguous-layout row->group index, the masked-layout valid-row counts and
+the no-padding layout's per-group row counts. It
 holds none of the GEMM's arithmetic; the GPU path and the CPU oracle both take
 its bytes as given.
 
@@ -169,6 +170,46 @@ class Masked:
                 + self.valid_rows() * (k + 4 * (k // BLOCK) + 2 * n) + 4 * self.num_groups)
 
 
+@dataclass
+class Nopad:
+    a: torch.Tensor          # [M, K]: the groups' rows back to back, then `tail` extra rows
+    sfa: torch.Tensor        # [K/128, tma_aligned(M)]
+    b: torch.Tensor          # [G, N, K]
+    sfb: torch.Tensor        # [G, N/128, K/128]
+    group_rows: torch.Tensor  # int32 [G]
+    rows: List[int]          # the counts as given (before any clipping)
+    m: int
+    n: int
+    k: int
+    num_groups: int
+
+    def new_output(self) -> torch.Tensor:
+        return sentinel_output((self.m, self.n), self.a.device)
+
+    def row_ranges(self) -> List[tuple]:
+        """[first, end) of each group: counts below zero count as zero, rows
+        at or past m do not exist."""
+        out, s = [], 0
+        for r in self.rows:
+            c = max(int(r), 0)
+            first = min(s, self.m)
+            out.append((first, min(first + c, self.m)))
+            s += c
+        return out
+
+    def valid_rows(self) -> int:
+        return int(sum(e - f for f, e in self.row_ranges()))
+
+    def flops(self) -> float:
+        return 2.0 * self.n * self.k * self.valid_rows()
+
+    def algorithmic_bytes(self) -> float:
+        n, k = self.n, self.k
+        used = sum(1 for f, e in self.row_ranges() if e > f)
+        return (used * (n * k + 4 * (n // BLOCK) * (k // BLOCK))
+                + self.valid_rows() * (k + 4 * (k // BLOCK) + 2 * n) + 4 * self.num_groups)
+
+
 def sentinel_output(shape, device) -> torch.Tensor:
     """A BF16 output buffer prefilled with the 0xFFFF sentinel."""
     return torch.full(shape, -1, dtype=torch.int16, device=device).view(torch.bfloat16)
@@ -228,8 +269,26 @@ def make_masked(counts: List[int], max_m: int, n: int, k: int, seed: int = 0, de
     return Masked(a, sfa, b, sfb, masked_m, list(map(int, counts)), max_m, n, k, num_groups)
 
 
+def make_nopad(rows: List[int], n: int, k: int, seed: int = 0, device="cpu", tail: int = 0,
+               m: Optional[int] = None, poison_tail: bool = False) -> Nopad:
+    """Groups' rows back to back with no padding, then `tail` rows that no
+    group owns (or exactly m rows when m is given)."""
+    if m is None:
+        m = int(sum(max(int(r), 0) for r in rows)) + tail
+    a, sfa = quantize_lhs(_randn((max(m, 1), k), seed, 1, device))
+    a = a[:m].contiguous()
+    sfa = sfa[:, :tma_aligned_size(m)].contiguous() if m else torch.zeros(k // BLOCK, 0, device=device)
+    b, sfb = _quantize_rhs_grouped(len(rows), n, k, seed, device)
+    group_rows = torch.tensor(list(rows), dtype=torch.int32, device=device)
+    w = Nopad(a, sfa, b, sfb, group_rows, list(map(int, rows)), m, n, k, len(rows))
+    if poison_tail and m:
+        used = max([e for _, e in w.row_ranges()], default=0)
+        a.view(torch.uint8)[used:] = 0x7F  # E4M3 NaN
+    return w
+
+
 # ---------------------------------------------------------------------------
-# The five benchmark workloads
+# The benchmark workloads
 # ---------------------------------------------------------------------------
 
 @dataclass
@@ -260,11 +319,12 @@ def zipf_rows(total: int, num_groups: int, s: float, seed: int) -> List[int]:
 
 
 def workload_spec(index: int, seed: int = 0) -> WorkloadSpec:
-    """The five workloads, indexed 0..4:
+    """The workloads, indexed 0..5:
     0 dense 128x256x512; 1 dense 4096x7168x2048;
     2 contiguous, 8 groups with rows uniform in [3000, 5000], N=4096, K=7168;
     3 masked decode, 16 groups, max_m=256, masked_m uniform in [1, 256], N=7168, K=2048;
-    4 contiguous, 32 groups with Zipf(1.2) rows totalling 65536, N=4096, K=7168.
+    4 contiguous, 32 groups with Zipf(1.2) rows totalling 65536, N=4096, K=7168;
+    5 no-padding layout of workload 2's groups (the same row counts, not padded).
     """
     if index == 0:
         return WorkloadSpec(0, "dense", "dense_128x256x512", n=256, k=512, m=128)
@@ -279,7 +339,13 @@ def workload_spec(index: int, seed: int = 0) -> WorkloadSpec:
     if index == 4:
         rows = zipf_rows(65536, 32, 1.2, seed)
         return WorkloadSpec(4, "contiguous", "contiguous_zipf1.2_32x65536_n4096_k7168", n=4096, k=7168, rows=rows)
+    if index == 5:
+        rows = [int(x) for x in _structure_rng(seed).integers(3000, 5001, size=8)]
+        return WorkloadSpec(5, "nopad", "nopad_8x[3000,5000]_n4096_k7168", n=4096, k=7168, rows=rows)
     raise ValueError(f"no workload {index}")
+
+
+NUM_WORKLOADS = 6
 
 
 def make_workload(spec: WorkloadSpec, seed: int = 0, device="cpu"):
@@ -289,6 +355,8 @@ def make_workload(spec: WorkloadSpec, seed: int = 0, device="cpu"):
         return make_contiguous(spec.rows, spec.n, spec.k, seed, device)
     if spec.kind == "masked":
         return make_masked(spec.counts, spec.max_m, spec.n, spec.k, seed, device)
+    if spec.kind == "nopad":
+        return make_nopad(spec.rows, spec.n, spec.k, seed, device)
     raise ValueError(spec.kind)
 
 

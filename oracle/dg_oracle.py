@@ -24,6 +24,9 @@ Sources on the pages:
     each is aligned to the M block size.
   * same page, "Grouped GEMMs (masked layout)": a per-group count of valid
     rows; only the valid part of each group is computed.
+  * same page, "Grouped GEMMs (nopad layout)": the groups' rows are
+    concatenated without alignment padding, and a tensor of per-group token
+    counts says where each group's rows are.
   * "DeepGEMM Compatibility Wrapper (deep-gemm)" page, "0.2.7 Compatibility
     Additions" and "Contiguous Grouped GEMM Alignment": scale recipe
     (1, 128, 128) and the 128-row segment alignment.
@@ -41,6 +44,11 @@ design notes of the repository):
     other id (-1 marks padding) leaves row m of D untouched.
   * masked layout: masked_m[g] is clamped to [0, max_m]; rows at or beyond it
     are left untouched.
+  * no-padding layout: the count tensor holds one int32 row count per group;
+    group 0's rows come first, then group 1's, and so on from row 0 of A and
+    D. A negative count counts as zero; rows at or past M do not exist, so a
+    group reaching past them is cut off there. Rows no group owns are left
+    untouched.
 """
 
 from __future__ import annotations
@@ -61,8 +69,11 @@ __all__ = [
     "fp8_gemm_nt",
     "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked",
+    "nopad_row_ranges",
+    "m_grouped_fp8_gemm_nt_nopad",
     "contiguous_f64_at",
     "masked_f64_at",
+    "nopad_f64_at",
 ]
 
 # Scale granularity along K for both operands: recipe (1, 128, 128).
@@ -237,6 +248,38 @@ def m_grouped_fp8_gemm_nt_masked(a_codes, sfa, b_codes, sfb, masked_m, d_init) -
     return d
 
 
+def nopad_row_ranges(group_rows, m_rows: int) -> list:
+    """[first, end) of each group's rows in the no-padding layout: the groups
+    follow one another from row 0, a negative count counts as zero, and
+    nothing lies at or past row m_rows."""
+    ranges, start = [], 0
+    for c in np.asarray(group_rows, dtype=np.int64):
+        first = min(start, m_rows)
+        end = min(start + max(int(c), 0), m_rows)
+        ranges.append((first, end))
+        start += max(int(c), 0)
+    return ranges
+
+
+def m_grouped_fp8_gemm_nt_nopad(a_codes, sfa, b_codes, sfb, group_rows, d_init) -> np.ndarray:
+    """M-grouped GEMM, no-padding layout.
+
+    a_codes [M, K], sfa [K/128, ld], b_codes [G, N, K], sfb [G, N/128, K/128],
+    group_rows int32 [G] (rows of each group), d_init uint16 [M, N].
+    Rows [first_g, end_g) of D (nopad_row_ranges) become
+    bf16(Ahat[r] . Bhat_g^T); all other rows keep d_init's contents.
+    """
+    m_rows = a_codes.shape[0]
+    d = np.array(d_init, dtype=np.uint16, copy=True)
+    for g, (first, end) in enumerate(nopad_row_ranges(group_rows, m_rows)):
+        if end == first:
+            continue
+        ahat = dequant_lhs(a_codes[first:end], sfa[:, first:end])
+        bhat = dequant_rhs(b_codes[g], sfb[g])
+        d[first:end] = bf16_bits(ahat @ bhat.T)
+    return d
+
+
 # ---------------------------------------------------------------------------
 # Sampled evaluation for full-size checks: a subset of rows and columns.
 # ---------------------------------------------------------------------------
@@ -285,4 +328,16 @@ def masked_f64_at(a_codes, sfa, b_codes, sfb, masked_m, group, rows, cols) -> np
     sel = np.nonzero(rows < valid)[0]
     if sel.size:
         out[sel] = _rows_cols_f64(a_codes[group], sfa[group], b_codes[group], sfb[group], rows[sel], cols)
+    return out
+
+
+def nopad_f64_at(a_codes, sfa, b_codes, sfb, group_rows, rows, cols) -> np.ndarray:
+    """Unrounded no-padding-layout result at rows x cols; NaN for rows that
+    no group owns."""
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.full((rows.size, len(cols)), np.nan)
+    for g, (first, end) in enumerate(nopad_row_ranges(group_rows, a_codes.shape[0])):
+        sel = np.nonzero((rows >= first) & (rows < end))[0]
+        if sel.size:
+            out[sel] = _rows_cols_f64(a_codes, sfa, b_codes[g], sfb[g], rows[sel], cols)
     return out

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = dg.lib()
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(n for n, _, _ in dg.SIGNATURES) == names
@@ -60,7 +60,14 @@ def _masked(a=A, sfa=SFA, b=B, sfb=SFB, d=D, mm=AUX, g=2, max_m=64, n=256, k=512
     return dg.lib().dg_m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, d, mm, g, max_m, n, k, None)
 
 
-@pytest.mark.parametrize("call", [_dense, _contig, _masked])
+def _nopad(a=A, sfa=SFA, b=B, sfb=SFB, d=D, rows=AUX, m=256, n=256, k=512, g=2):
+    return dg.lib().dg_m_grouped_fp8_gemm_nt_nopad(a, sfa, b, sfb, d, rows, m, n, k, g, None)
+
+
+CALLS = [_dense, _contig, _masked, _nopad]
+
+
+@pytest.mark.parametrize("call", CALLS)
 def test_null_pointers(call):
     for arg in ("a", "sfa", "b", "sfb", "d"):
         assert call(**{arg: None}) == 1
@@ -68,9 +75,11 @@ def test_null_pointers(call):
         assert call(lay=None) == 1
     if call is _masked:
         assert call(mm=None) == 1
+    if call is _nopad:
+        assert call(rows=None) == 1
 
 
-@pytest.mark.parametrize("call", [_dense, _contig, _masked])
+@pytest.mark.parametrize("call", CALLS)
 def test_shapes(call):
     assert call(n=0) == 2
     assert call(n=-128) == 2
@@ -101,7 +110,15 @@ def test_masked_shapes():
     assert _masked(g=0) == 0
 
 
-@pytest.mark.parametrize("call", [_dense, _contig, _masked])
+def test_nopad_shapes():
+    assert _nopad(m=-1) == 2
+    assert _nopad(g=-1) == 2
+    assert _nopad(g=2049) == 4
+    assert _nopad(m=0) == 0          # empty: successful no-ops
+    assert _nopad(g=0) == 0
+
+
+@pytest.mark.parametrize("call", CALLS)
 def test_alignment(call):
     for arg, val in (("a", A + 8), ("b", B + 4), ("d", D + 2), ("sfa", SFA + 4), ("sfb", SFB + 8)):
         assert call(**{arg: val}) == 3

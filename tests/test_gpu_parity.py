@@ -1,7 +1,7 @@
 """GPU parity: the gfx950 kernels against the CPU oracle, through the C ABI.
 
 Small shapes (several tiles, ragged tails, empty groups) are compared in
-full; the five benchmark workloads at full size are compared on sampled
+full; the benchmark workloads at full size are compared on sampled
 rows and columns, plus the invariant that no row outside the valid rows is
 written. Integer-exact inputs are compared bit for bit.
 """
@@ -253,8 +253,121 @@ def test_masked_graph_replay_follows_device_counts(dev):
         _check_masked(w, d, counts, f"graph {counts}")
 
 
+def test_masked_many_groups(dev):
+    """More groups than one 64-wide pass of the on-device group table."""
+    rng = np.random.default_rng(31)
+    counts = [int(c) for c in rng.integers(0, 40, size=150)]
+    counts[64] = 0
+    counts[127] = 33
+    _say(f"masked {len(counts)} groups")
+    w = synth.make_masked(counts, 40, 128, 256, seed=4, device=dev, poison_invalid=True)
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m)
+    torch.cuda.synchronize()
+    _check_masked(w, d, counts, "masked many groups")
+
+
 # ---------------------------------------------------------------------------
-# The five benchmark workloads at full size (sampled comparison)
+# No-padding layout
+# ---------------------------------------------------------------------------
+
+def _check_nopad(w, d, what):
+    got = NP(d)
+    owned = np.zeros(w.m, bool)
+    for g, (first, end) in enumerate(O.nopad_row_ranges(NP(w.group_rows), w.m)):
+        if end > first:
+            ref = O.dense_f64_at(NP(w.a), NP(w.sfa), NP(w.b)[g], NP(w.sfb)[g], np.arange(first, end),
+                                 np.arange(w.n))
+            check_close(got[first:end], ref, f"{what} group {g}")
+            owned[first:end] = True
+    check_untouched(got[~owned], what + " rows no group owns")
+
+
+@pytest.mark.parametrize("rows,n,k,tail", [
+    ([130, 0, 77, 256, 1], 256, 512, 7),
+    ([1], 128, 128, 0),
+    ([5, 300, 1, 129], 384, 1024, 3),
+    ([130, 0, 77, 256, 1], 896, 512, 0),
+    ([130, 0, 77, 256, 1], 256, 4096, 5),
+])
+def test_nopad_small(dev, rows, n, k, tail):
+    _say(f"nopad rows={rows} n={n} k={k} tail={tail}")
+    w = synth.make_nopad(rows, n, k, seed=len(rows) + tail, device=dev, tail=tail, poison_tail=True)
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows)
+    torch.cuda.synchronize()
+    _check_nopad(w, d, f"nopad {rows}")
+
+
+def test_nopad_many_groups(dev):
+    """Groups of 0-6 rows, more than one 64-wide pass of the group table."""
+    rng = np.random.default_rng(37)
+    rows = [int(c) for c in rng.integers(0, 7, size=300)]
+    _say(f"nopad {len(rows)} groups, {sum(rows)} rows")
+    w = synth.make_nopad(rows, 128, 256, seed=6, device=dev, tail=9, poison_tail=True)
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows)
+    torch.cuda.synchronize()
+    _check_nopad(w, d, "nopad many groups")
+
+
+def test_nopad_clips_counts(dev):
+    """A negative count owns nothing; counts reaching past M are cut off."""
+    _say("nopad clipped counts")
+    w = synth.make_nopad([-3, 100, 50, 7], 256, 512, seed=8, device=dev, m=120)
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows)
+    torch.cuda.synchronize()
+    assert O.nopad_row_ranges(NP(w.group_rows), w.m) == [(0, 0), (0, 100), (100, 120), (120, 120)]
+    _check_nopad(w, d, "nopad clipped")
+
+
+def test_nopad_equals_dense_per_group(dev):
+    """Same kernel arithmetic, so a group's rows match a dense call on them bit for bit."""
+    w = synth.make_nopad([200, 1, 383, 0, 130], 512, 1024, seed=10, device=dev)
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows)
+    for g, (first, end) in enumerate(w.row_ranges()):
+        if end == first:
+            continue
+        a_g = w.a[first:end].contiguous()
+        sfa_g = torch.zeros(w.k // 128, synth.tma_aligned_size(end - first), dtype=torch.float32, device=dev)
+        sfa_g[:, :end - first] = w.sfa[:, first:end]
+        d_g = synth.sentinel_output((end - first, w.n), dev)
+        dg.fp8_gemm_nt(a_g, sfa_g, w.b[g].contiguous(), w.sfb[g].contiguous(), d_g)
+        torch.cuda.synchronize()
+        assert torch.equal(d[first:end].view(torch.int16), d_g.view(torch.int16)), f"group {g}"
+
+
+def test_nopad_graph_replay_follows_device_counts(dev):
+    """One captured graph serves changing group_rows contents; replays are
+    checked against eager calls, with eager work between replays."""
+    w = synth.make_nopad([100, 50, 7, 64], 256, 512, seed=12, device=dev, tail=35)
+    d = w.new_output()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        dg.m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows)  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dg.m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows)
+    for rows in ([100, 50, 7, 64], [0, 256, 0, 0], [1, 1, 1, 300]):
+        w.group_rows.copy_(torch.tensor(rows, dtype=torch.int32))
+        w.rows = list(rows)
+        d.view(torch.int16).fill_(-1)
+        graph.replay()
+        torch.cuda.synchronize()
+        d_eager = w.new_output()
+        dg.m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d_eager, w.group_rows)
+        torch.cuda.synchronize()
+        assert torch.equal(d.view(torch.int16), d_eager.view(torch.int16)), rows
+        _check_nopad(w, d, f"graph {rows}")
+
+
+# ---------------------------------------------------------------------------
+# The benchmark workloads at full size (sampled comparison)
 # ---------------------------------------------------------------------------
 
 def _sample(n_total, count, rng, extra=()):
@@ -263,7 +376,7 @@ def _sample(n_total, count, rng, extra=()):
     return np.array(sorted(idx), dtype=np.int64)
 
 
-@pytest.mark.parametrize("index", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("index", list(range(synth.NUM_WORKLOADS)))
 def test_workload_full_size(dev, index):
     spec = synth.workload_spec(index)
     _say(f"workload {index} {spec.name}")
@@ -289,6 +402,17 @@ def test_workload_full_size(dev, index):
         ref = O.contiguous_f64_at(a, sfa, b, sfb, layout, rows, cols)
         check_close(got[np.ix_(rows, cols)], ref, spec.name)
         check_untouched(got[layout < 0], spec.name + " padding rows")
+    elif spec.kind == "nopad":
+        group_rows = NP(w.group_rows)
+        ranges = O.nopad_row_ranges(group_rows, w.m)
+        firsts = [f for f, e in ranges if e > f]
+        lasts = [e - 1 for f, e in ranges if e > f]
+        rows = _sample(w.m, 128, rng, firsts + lasts)
+        cols = _sample(w.n, 64, rng, (0, 127, 128, w.n - 1))
+        ref = O.nopad_f64_at(a, sfa, b, sfb, group_rows, rows, cols)
+        check_close(got[np.ix_(rows, cols)], ref, spec.name)
+        used = max(lasts) + 1
+        check_untouched(got[used:], spec.name + " rows no group owns")
     else:
         counts = w.counts
         for g in range(w.num_groups):

@@ -9,12 +9,16 @@ Each pin checks the oracle against something other than its own code:
   * all scales 1: torch float64 matmul of the decoded operands;
   * constant operands: a closed form in the scales alone;
   * invariants: grouped == per-group dense, permuting segments permutes rows,
-    masked and padding rows untouched, NaN-poisoned padding does not leak.
+    masked and padding rows untouched, NaN-poisoned padding does not leak,
+    the no-padding layout with 128-aligned counts == the contiguous layout;
+  * a no-padding row owner map built by walking the counts row by row.
 
 test_planted_mistakes_are_caught plants plausible mistakes in a private copy
 of the oracle (wrong scale index, transposed RHS scales, wrong FP8 flavour,
 truncating or double rounding, dropped K block, missing sign, padding rows
-written, off-by-one masks) and checks that at least one pin fails for each.
+written, off-by-one masks, no-padding groups that restart at row 0, negative
+counts that move later groups back, unowned rows written) and checks that at
+least one pin fails for each.
 """
 
 import importlib.util
@@ -258,6 +262,79 @@ def pin_masked_rows(orc):
     assert np.array_equal(d2[1:3], d[1:3]) and np.all(d2[0] == 0xFFFF)
 
 
+def _nopad_owner(counts, m_rows):
+    """Group of each row of the no-padding layout, walked row by row: group
+    g's max(c_g, 0) rows follow group g - 1's; rows no group reaches, and
+    anything past m_rows, are -1."""
+    owner = []
+    for g, c in enumerate(counts):
+        owner.extend([g] * max(int(c), 0))
+    owner = owner[:m_rows]
+    return np.array(owner + [-1] * (m_rows - len(owner)), dtype=np.int64)
+
+
+def pin_exact_nopad(orc):
+    """Tiny no-padding case against exact rationals, with a row owner map
+    built by walking the counts one row at a time."""
+    rng = np.random.default_rng(23)
+    counts = [2, 0, 3, -1]
+    m_rows = 7                      # rows 5 and 6 belong to no group
+    a, sfa, b, sfb = _random_inputs(rng, m_rows, 128, 256, groups=len(counts))
+    owner = _nopad_owner(counts, m_rows)
+    d0 = np.full((m_rows, 128), 0xFFFF, dtype=np.uint16)
+    d = orc.m_grouped_fp8_gemm_nt_nopad(a, sfa, b, sfb, np.array(counts, np.int32), d0)
+    for r in range(m_rows):
+        g = int(owner[r])
+        if g < 0:
+            assert np.all(d[r] == 0xFFFF), r
+            continue
+        sub_sfa = np.pad(sfa[:, [r]], ((0, 0), (0, 3)))
+        exact, _, _ = _exact_gemm(a[[r]], sub_sfa, b[g], sfb[g])
+        for j in range(128):
+            ex = exact[0][j]
+            assert int(d[r, j]) == _bf16_rne_exact(ex) or abs(
+                float(O.bf16_bits_to_f64(d[r, j])) - float(ex)) <= 2.0 ** -7 * abs(float(ex)), (r, j)
+
+
+def pin_nopad_layout_invariants(orc):
+    """No-padding rows: (1) 128-aligned counts give the contiguous layout's
+    result on the same rows; (2) each group equals a dense call on its rows;
+    (3) counts past M are cut off at M and negative counts own nothing;
+    (4) NaN-poisoned rows that no group owns never leak."""
+    rng = np.random.default_rng(29)
+    counts = [128, 0, 256]
+    m_rows = 384
+    a, sfa, b, sfb = _random_inputs(rng, m_rows, 128, 256, groups=3)
+    d0 = np.full((m_rows, 128), 0xFFFF, np.uint16)
+    layout = np.r_[np.zeros(128), np.full(256, 2)].astype(np.int32)
+    d_np = orc.m_grouped_fp8_gemm_nt_nopad(a, sfa, b, sfb, np.array(counts, np.int32), d0)
+    d_ct = orc.m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, layout, d0)
+    assert np.array_equal(d_np, d_ct)
+
+    counts = [-4, 5, 0, 9, 100]
+    m_rows = 20
+    a, sfa, b, sfb = _random_inputs(rng, m_rows, 128, 256, groups=len(counts))
+    d0 = np.full((m_rows, 128), 0xFFFF, np.uint16)
+    d = orc.m_grouped_fp8_gemm_nt_nopad(a, sfa, b, sfb, np.array(counts, np.int32), d0)
+    owner = _nopad_owner(counts, m_rows)
+    assert list(owner[:5]) == [1] * 5 and list(owner[5:14]) == [3] * 9 and list(owner[14:]) == [4] * 6
+    for g in range(len(counts)):
+        rows = np.nonzero(owner == g)[0]
+        if rows.size == 0:
+            continue
+        sub_sfa = np.pad(sfa[:, rows], ((0, 0), (0, (-rows.size) % 4)))
+        assert np.array_equal(d[rows], orc.fp8_gemm_nt(a[rows], sub_sfa, b[g], sfb[g])), g
+
+    counts = [3, 4]
+    m_rows = 12
+    a, sfa, b, sfb = _random_inputs(rng, m_rows, 128, 256, groups=2)
+    a[7:] = 0x7F
+    d0 = np.full((m_rows, 128), 0xFFFF, np.uint16)
+    d = orc.m_grouped_fp8_gemm_nt_nopad(a, sfa, b, sfb, np.array(counts, np.int32), d0)
+    assert np.all(d[7:] == 0xFFFF)
+    assert not np.any(np.isnan(O.bf16_bits_to_f64(d[:7])))
+
+
 def pin_contiguous_poisoned_padding(orc):
     rng = np.random.default_rng(17)
     rows = [5, 128, 1]
@@ -319,6 +396,8 @@ PINS = [
     pin_masked_rows,
     pin_contiguous_poisoned_padding,
     pin_sampled_matches_full,
+    pin_exact_nopad,
+    pin_nopad_layout_invariants,
 ]
 
 
@@ -434,6 +513,37 @@ def _mut_lhs_scale_by_k_only(mod):
     mod.dequant_lhs = f
 
 
+def _mut_nopad_groups_restart(mod):
+    # every group starts at row 0 (offsets dropped)
+    def f(group_rows, m_rows):
+        return [(0, min(max(int(c), 0), m_rows)) for c in np.asarray(group_rows)]
+    mod.nopad_row_ranges = f
+
+
+def _mut_nopad_negative_counts(mod):
+    # negative counts move the next group's start backwards
+    def f(group_rows, m_rows):
+        out, s = [], 0
+        for c in np.asarray(group_rows, np.int64):
+            first = min(max(s, 0), m_rows)
+            out.append((first, min(max(first + int(c), first), m_rows)))
+            s += int(c)
+        return out
+    mod.nopad_row_ranges = f
+
+
+def _mut_nopad_last_group_to_end(mod):
+    # the last group also takes the rows no group owns
+    orig = mod.nopad_row_ranges
+
+    def f(group_rows, m_rows):
+        r = orig(group_rows, m_rows)
+        if r:
+            r[-1] = (r[-1][0], m_rows)
+        return r
+    mod.nopad_row_ranges = f
+
+
 MUTANTS = [
     _mut_lhs_scale_first_row,
     _mut_rhs_scale_transposed,
@@ -445,6 +555,9 @@ MUTANTS = [
     _mut_padding_written,
     _mut_masked_off_by_one,
     _mut_lhs_scale_by_k_only,
+    _mut_nopad_groups_restart,
+    _mut_nopad_negative_counts,
+    _mut_nopad_last_group_to_end,
 ]
 
 
