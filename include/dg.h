@@ -140,6 +140,39 @@ dg_status dg_m_grouped_fp8_gemm_nt_nopad(const void* a, const float* sfa,
                                          int m, int n, int k, int num_groups,
                                          void* stream);
 
+/*
+ * The four GEMMs above with power-of-two scales applied by the matrix cores
+ * ("DeepGEMM Compatibility Wrapper" page, "0.2.7 Compatibility Additions":
+ * UE8M0 scale casting and the packed UE8M0 scale conversion). Arguments,
+ * layouts and checks are exactly those of the call without the suffix. The
+ * scales are meant to be positive normal powers of two, as a UE8M0 cast at
+ * quantisation makes them; each float32 scale s is used as 2^(e - 127),
+ * e being its biased exponent field (bits 30..23), which is s itself for
+ * such a value (sign and mantissa bits are ignored, as in the packed UE8M0
+ * conversion; e = 255 gives NaN). The per-block scales are applied inside
+ * the MFMA as E8M0 block scales and the products accumulate in float32 in
+ * the MFMA, so there is no separate promotion step.
+ */
+dg_status dg_fp8_gemm_nt_ue8m0(const void* a, const float* sfa,
+                               const void* b, const float* sfb,
+                               void* d,
+                               int m, int n, int k, void* stream);
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* a, const float* sfa,
+                                                    const void* b, const float* sfb,
+                                                    void* d, const int32_t* grouped_layout,
+                                                    int m, int n, int k, int num_groups,
+                                                    void* stream);
+dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void* a, const float* sfa,
+                                                const void* b, const float* sfb,
+                                                void* d, const int32_t* masked_m,
+                                                int num_groups, int max_m, int n, int k,
+                                                void* stream);
+dg_status dg_m_grouped_fp8_gemm_nt_nopad_ue8m0(const void* a, const float* sfa,
+                                               const void* b, const float* sfb,
+                                               void* d, const int32_t* group_rows,
+                                               int m, int n, int k, int num_groups,
+                                               void* stream);
+
 /* Row alignment of each group's segment in the contiguous layout: 128
  * ("DeepGEMM Compatibility Wrapper" page, "Contiguous Grouped GEMM
  * Alignment"; "DeepGEMM for PPU" README, "Utilities"). */

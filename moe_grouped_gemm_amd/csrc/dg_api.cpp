@@ -48,19 +48,16 @@ dg_status common_checks(const void* a, const float* sfa, const void* b, const fl
   return DG_OK;
 }
 
-dg_status launch(int kind, dg::GemmArgs& args, void* stream) {
+dg_status launch(int kind, dg::GemmArgs& args, bool e8m0, void* stream) {
+  args.scale_e8m0 = e8m0 ? 1 : 0;
   const int cus = effective_cus();
   if (cus <= 0) return DG_ERR_DEVICE;
   hipError_t e = dg::launch_gemm(kind, args, cus, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? DG_OK : DG_ERR_LAUNCH;
 }
 
-}  // namespace
-
-extern "C" {
-
-dg_status dg_fp8_gemm_nt(const void* a, const float* sfa, const void* b, const float* sfb, void* d, int m, int n,
-                         int k, void* stream) {
+dg_status dense(const void* a, const float* sfa, const void* b, const float* sfb, void* d, int m, int n, int k,
+                bool e8m0, void* stream) {
   if (dg_status s = common_checks(a, sfa, b, sfb, d, n, k)) return s;
   if (m < 0) return DG_ERR_SHAPE;
   if ((long long)m * k >= kMaxBytes || (long long)m * n * 2 >= kMaxBytes || (long long)n * k >= kMaxBytes)
@@ -78,12 +75,11 @@ dg_status dg_fp8_gemm_nt(const void* a, const float* sfa, const void* b, const f
   args.k = k;
   args.num_groups = 1;
   args.ld_sfa = tma_aligned(m, 4);
-  return launch(dg::KIND_DENSE, args, stream);
+  return launch(dg::KIND_DENSE, args, e8m0, stream);
 }
 
-dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, const void* b, const float* sfb,
-                                              void* d, const int32_t* grouped_layout, int m, int n, int k,
-                                              int num_groups, void* stream) {
+dg_status contiguous(const void* a, const float* sfa, const void* b, const float* sfb, void* d,
+                     const int32_t* grouped_layout, int m, int n, int k, int num_groups, bool e8m0, void* stream) {
   if (dg_status s = common_checks(a, sfa, b, sfb, d, n, k)) return s;
   if (!grouped_layout) return DG_ERR_NULL;
   if (m < 0 || num_groups < 0 || m % 128 != 0) return DG_ERR_SHAPE;
@@ -103,12 +99,11 @@ dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, c
   args.k = k;
   args.num_groups = num_groups;
   args.ld_sfa = tma_aligned(m, 4);
-  return launch(dg::KIND_CONTIGUOUS, args, stream);
+  return launch(dg::KIND_CONTIGUOUS, args, e8m0, stream);
 }
 
-dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, const void* b, const float* sfb, void* d,
-                                          const int32_t* masked_m, int num_groups, int max_m, int n, int k,
-                                          void* stream) {
+dg_status masked(const void* a, const float* sfa, const void* b, const float* sfb, void* d, const int32_t* masked_m,
+                 int num_groups, int max_m, int n, int k, bool e8m0, void* stream) {
   if (dg_status s = common_checks(a, sfa, b, sfb, d, n, k)) return s;
   if (!masked_m) return DG_ERR_NULL;
   if (num_groups < 0 || max_m <= 0) return DG_ERR_SHAPE;
@@ -129,12 +124,11 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, const
   args.k = k;
   args.num_groups = num_groups;
   args.ld_sfa = tma_aligned(max_m, 4);
-  return launch(dg::KIND_MASKED, args, stream);
+  return launch(dg::KIND_MASKED, args, e8m0, stream);
 }
 
-dg_status dg_m_grouped_fp8_gemm_nt_nopad(const void* a, const float* sfa, const void* b, const float* sfb, void* d,
-                                         const int32_t* group_rows, int m, int n, int k, int num_groups,
-                                         void* stream) {
+dg_status nopad(const void* a, const float* sfa, const void* b, const float* sfb, void* d, const int32_t* group_rows,
+                int m, int n, int k, int num_groups, bool e8m0, void* stream) {
   if (dg_status s = common_checks(a, sfa, b, sfb, d, n, k)) return s;
   if (!group_rows) return DG_ERR_NULL;
   if (m < 0 || num_groups < 0) return DG_ERR_SHAPE;
@@ -155,7 +149,57 @@ dg_status dg_m_grouped_fp8_gemm_nt_nopad(const void* a, const float* sfa, const 
   args.k = k;
   args.num_groups = num_groups;
   args.ld_sfa = tma_aligned(m, 4);
-  return launch(dg::KIND_NOPAD, args, stream);
+  return launch(dg::KIND_NOPAD, args, e8m0, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_fp8_gemm_nt(const void* a, const float* sfa, const void* b, const float* sfb, void* d, int m, int n,
+                         int k, void* stream) {
+  return dense(a, sfa, b, sfb, d, m, n, k, false, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, const void* b, const float* sfb,
+                                              void* d, const int32_t* grouped_layout, int m, int n, int k,
+                                              int num_groups, void* stream) {
+  return contiguous(a, sfa, b, sfb, d, grouped_layout, m, n, k, num_groups, false, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, const void* b, const float* sfb, void* d,
+                                          const int32_t* masked_m, int num_groups, int max_m, int n, int k,
+                                          void* stream) {
+  return masked(a, sfa, b, sfb, d, masked_m, num_groups, max_m, n, k, false, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_nopad(const void* a, const float* sfa, const void* b, const float* sfb, void* d,
+                                         const int32_t* group_rows, int m, int n, int k, int num_groups,
+                                         void* stream) {
+  return nopad(a, sfa, b, sfb, d, group_rows, m, n, k, num_groups, false, stream);
+}
+
+dg_status dg_fp8_gemm_nt_ue8m0(const void* a, const float* sfa, const void* b, const float* sfb, void* d, int m,
+                               int n, int k, void* stream) {
+  return dense(a, sfa, b, sfb, d, m, n, k, true, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* a, const float* sfa, const void* b,
+                                                    const float* sfb, void* d, const int32_t* grouped_layout, int m,
+                                                    int n, int k, int num_groups, void* stream) {
+  return contiguous(a, sfa, b, sfb, d, grouped_layout, m, n, k, num_groups, true, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void* a, const float* sfa, const void* b, const float* sfb,
+                                                void* d, const int32_t* masked_m, int num_groups, int max_m, int n,
+                                                int k, void* stream) {
+  return masked(a, sfa, b, sfb, d, masked_m, num_groups, max_m, n, k, true, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_nopad_ue8m0(const void* a, const float* sfa, const void* b, const float* sfb,
+                                               void* d, const int32_t* group_rows, int m, int n, int k,
+                                               int num_groups, void* stream) {
+  return nopad(a, sfa, b, sfb, d, group_rows, m, n, k, num_groups, true, stream);
 }
 
 int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }

@@ -67,6 +67,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// The E8M0 code of a float32 scale: its biased exponent field e, which the
+// MFMA's block-scale operand reads as 2^(e - 127) (e = 255: NaN). For a
+// positive normal power of two this is the scale itself; sign and mantissa
+// bits are ignored.
+__device__ __forceinline__ int e8m0_code(float s) {
+  return (int)((__builtin_bit_cast(uint32_t, s) >> 23) & 0xFFu);
+}
+
 // Where one output tile's operands live, and which of its rows are valid.
 struct TileRef {
   const uint8_t* a;    // row 0 of the group's A

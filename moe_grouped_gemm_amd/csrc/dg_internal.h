@@ -32,6 +32,8 @@ struct GemmArgs {
   int m;               // dense/contiguous/no-padding: rows of A and D; masked: max_m
   int n, k, num_groups;
   int ld_sfa;          // leading dimension of the transposed LHS scales
+  int scale_e8m0;      // nonzero: every scale is used as 2^(its exponent field - 127), applied
+                       // by the MFMA itself (E8M0 block scales) instead of a float32 promotion
   int m_blocks, n_blocks, num_tiles;  // filled in by launch_gemm
 };
 

@@ -315,7 +315,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& cur
 //              refill of stage s (step g + 2) are issued.
 // The MFMAs issued before the barrier keep the matrix core busy while the
 // waves meet, and every step starts with its operands in registers.
-template <class C, int KIND, int PHASE>
+template <class C, int KIND, int PHASE, bool E8>
 __device__ __forceinline__ void mainloop(const GemmArgs& p, const TileSrc& t0, const TileSrc& t1, const TileSrc& t2,
                                          WaveTile<C>& wt, float (&sbv)[2], int wave, const LdsOffsets& lds,
                                          const LaneOffsets& lo, const RowGroups& nrg, int ngroup, RowMask& nmask) {
@@ -351,6 +351,7 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const TileSrc& t0, c
       const StageSrc r1 = refill_src(t0, t1, t2, kb + 1, p, k_blocks);
       const StageSrc r2 = refill_src(t0, t1, t2, kb + 2, p, k_blocks);
       const float sb = sbv[s];  // this step's RHS scale, loaded with its stage
+      [[maybe_unused]] const int eb = e8m0_code(sb);
       if (!wt.on) {
         issue_part<C, sn, 2>(r1, wave, lo);
         sbv[sn] = issue_part<C, sn, 3>(r1, wave, lo);
@@ -369,31 +370,51 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const TileSrc& t0, c
         sav[(mt + 2) % 4] = sa_at<C, s>(lds.sa, mt + 2);
         if (mt == 0) issue_part<C, sn, 2>(r1, wave, lo);
         if (mt == 1) sbv[sn] = issue_part<C, sn, 3>(r1, wave, lo);
-        f32x4 part[C::NT];
+        if constexpr (E8) {
+          // Power-of-two scales: the MFMA applies them and accumulates.
+          const int ea = e8m0_code(sav[mt % 4]);
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt)
-          part[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[mt % 4], (f32x4){0.f, 0.f, 0.f, 0.f},
-                                                                     0, 0, 0, 0, 0, 0);
-        const float w = sav[mt % 4] * sb;
+          for (int nt = 0; nt < C::NT; ++nt)
+            wt.acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[mt % 4], wt.acc[mt][nt],
+                                                                             0, 0, 0, eb, 0, ea);
+        } else {
+          f32x4 part[C::NT];
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) wt.acc[mt][nt] += part[nt] * w;
+          for (int nt = 0; nt < C::NT; ++nt)
+            part[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[mt % 4],
+                                                                       (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+          const float w = sav[mt % 4] * sb;
+#pragma unroll
+          for (int nt = 0; nt < C::NT; ++nt) wt.acc[mt][nt] += part[nt] * w;
+        }
         // Issue order: the reads two bands ahead and this band's share of
         // the refill first, then the MFMAs, then the promotion.
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS reads
         if (mt == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM loads
         if (mt == 1) __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+        if constexpr (E8) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU: the scale code
         __builtin_amdgcn_sched_group_barrier(0x008, C::NT, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 4 * C::NT + 1, 0);  // VALU
+        if constexpr (!E8) __builtin_amdgcn_sched_group_barrier(0x002, 4 * C::NT + 1, 0);  // VALU
         __builtin_amdgcn_sched_barrier(0);
       }
       const float w6 = sav[6 % 4] * sb;
       const float w7 = sav[7 % 4] * sb;
+      [[maybe_unused]] const int ea6 = e8m0_code(sav[6 % 4]);
+      [[maybe_unused]] const int ea7 = e8m0_code(sav[7 % 4]);
 #pragma unroll
       for (int nt = 0; nt < C::NT; ++nt) {
-        const f32x4 p6 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[6 % 4],
-                                                                         (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-        const f32x4 p7 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[7 % 4],
-                                                                         (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        f32x4 p6, p7;
+        if constexpr (E8) {
+          wt.acc[6][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[6 % 4], wt.acc[6][nt],
+                                                                          0, 0, 0, eb, 0, ea6);
+          wt.acc[7][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[7 % 4], wt.acc[7][nt],
+                                                                          0, 0, 0, eb, 0, ea7);
+        } else {
+          p6 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[6 % 4], (f32x4){0.f, 0.f, 0.f, 0.f},
+                                                               0, 0, 0, 0, 0, 0);
+          p7 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[7 % 4], (f32x4){0.f, 0.f, 0.f, 0.f},
+                                                               0, 0, 0, 0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if (nt == 0) {
           wait_lgkmcnt_0();
@@ -415,15 +436,17 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const TileSrc& t0, c
           af[1] = frag_at<C, sn>(lds.a0, lds.a1, 1);
           sav[1] = sa_at<C, sn>(lds.sa, 1);
         }
-        wt.acc[6][nt] += p6 * w6;
-        wt.acc[7][nt] += p7 * w7;
+        if constexpr (!E8) {
+          wt.acc[6][nt] += p6 * w6;
+          wt.acc[7][nt] += p7 * w7;
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     });
   }
 }
 
-template <class C, int KIND>
+template <class C, int KIND, bool E8>
 __global__ void __launch_bounds__(C::THREADS, 1) fp8_gemm_nt_kernel(GemmArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -506,8 +529,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) fp8_gemm_nt_kernel(GemmArgs p) 
 #pragma unroll
       for (int nt = 0; nt < C::NT; ++nt) wt.acc[mt][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    if (phase == 0) mainloop<C, KIND, 0>(p, c0, c1, c2, wt, sbv, wave, lds, lo, nrg, nxt.group, nmask);
-    else mainloop<C, KIND, 1>(p, c0, c1, c2, wt, sbv, wave, lds, lo, nrg, nxt.group, nmask);
+    if (phase == 0) mainloop<C, KIND, 0, E8>(p, c0, c1, c2, wt, sbv, wave, lds, lo, nrg, nxt.group, nmask);
+    else mainloop<C, KIND, 1, E8>(p, c0, c1, c2, wt, sbv, wave, lds, lo, nrg, nxt.group, nmask);
     phase = (phase + k_blocks) % C::STAGES;
 
     // Epilogue (the next tile's first K block has landed, its second is in
@@ -541,7 +564,7 @@ using CfgLarge = Config<256, 256, 2, 4, 2>;
 
 template <class C, int KIND>
 static hipError_t launch(const GemmArgs& args, int num_cus, hipStream_t stream) {
-  auto kern = fp8_gemm_nt_kernel<C, KIND>;
+  auto kern = args.scale_e8m0 ? fp8_gemm_nt_kernel<C, KIND, true> : fp8_gemm_nt_kernel<C, KIND, false>;
   int per_cu = 1;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, C::THREADS, 0);
   if (e != hipSuccess) return e;

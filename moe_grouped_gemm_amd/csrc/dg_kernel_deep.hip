@@ -386,21 +386,39 @@ __device__ __forceinline__ void read_first(Operands<C>& o, const LdsOffsets& lds
 // before each barrier keep the matrix core busy while the waves meet.
 constexpr int BAND_A = 2;  // band of barrier 1
 
-template <class C, int S>
+// The MFMAs of band mt. Float32 scales: the partial sums of the K block go
+// to `part`, promoted by the caller. Power-of-two scales (E8): the MFMA
+// applies them as E8M0 block scales (eb for the B fragments, this band's ea
+// for the A fragment) and accumulates into the totals itself.
+template <class C, bool E8, int MT>
+__device__ __forceinline__ void band_mfmas(WaveTile<C>& wt, f32x4 (&part)[C::NT], const Operands<C>& o, int eb) {
+  if constexpr (E8) {
+    const int ea = e8m0_code(o.sav[MT % 4]);
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt)
+      wt.acc[MT][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[MT % 4], wt.acc[MT][nt],
+                                                                       0, 0, 0, eb, 0, ea);
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt)
+      part[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[MT % 4], (f32x4){0.f, 0.f, 0.f, 0.f},
+                                                                 0, 0, 0, 0, 0, 0);
+  }
+}
+
+template <class C, int S, bool E8>
 __device__ __forceinline__ void step_on(WaveTile<C>& wt, Operands<C>& o, const StageSrc& r2, int wave, int lane,
                                         const LdsOffsets& lds, const LaneOffsets& lo) {
   static_assert(C::MT == 8 && C::NT == 4, "pipeline shape");
   constexpr int SN = 1 - S;
   constexpr int IN_FLIGHT = C::X_LOADS + C::Y_LOADS;
   const float sb = o.sb;
+  [[maybe_unused]] const int eb = e8m0_code(sb);
   static_for<0, 6>([&](auto mi) {
     constexpr int mt = decltype(mi)::value;
     f32x4 part[C::NT];
     if constexpr (mt == BAND_A) {
-#pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt)
-        part[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[mt % 4],
-                                                                   (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+      band_mfmas<C, E8, mt>(wt, part, o, eb);
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<IN_FLIGHT>();
       wait_lgkmcnt_0();
@@ -409,40 +427,52 @@ __device__ __forceinline__ void step_on(WaveTile<C>& wt, Operands<C>& o, const S
       o.af[(mt + 2) % 4] = frag_a<C, S, mt + 2>(lds);
       o.sav[(mt + 2) % 4] = sa_at<C, S, mt + 2>(lds);
       issue_x<C, S, 0>(r2, wave, lane, lo);
-      const float w = o.sav[mt % 4] * sb;
+      if constexpr (!E8) {
+        const float w = o.sav[mt % 4] * sb;
 #pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt) wt.acc[mt][nt] += part[nt] * w;
+        for (int nt = 0; nt < C::NT; ++nt) wt.acc[mt][nt] += part[nt] * w;
+      }
       __builtin_amdgcn_sched_barrier(0);
     } else {
       o.af[(mt + 2) % 4] = frag_a<C, S, mt + 2>(lds);
       o.sav[(mt + 2) % 4] = sa_at<C, S, mt + 2>(lds);
       if constexpr (mt == BAND_A + 1) issue_x<C, S, 1>(r2, wave, lane, lo);
       if constexpr (mt == BAND_A + 2) issue_x<C, S, 2>(r2, wave, lane, lo);
+      band_mfmas<C, E8, mt>(wt, part, o, eb);
+      if constexpr (!E8) {
+        const float w = o.sav[mt % 4] * sb;
 #pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt)
-        part[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[mt % 4],
-                                                                   (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-      const float w = o.sav[mt % 4] * sb;
-#pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt) wt.acc[mt][nt] += part[nt] * w;
+        for (int nt = 0; nt < C::NT; ++nt) wt.acc[mt][nt] += part[nt] * w;
+      }
       // Issue order: the reads two bands ahead and this band's share of the
       // refill first, then the MFMAs, then the promotion.
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS reads
       if constexpr (mt == BAND_A + 1) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM loads
       if constexpr (mt == BAND_A + 2) __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+      if constexpr (E8) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU: the scale code
       __builtin_amdgcn_sched_group_barrier(0x008, C::NT, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 4 * C::NT + 1, 0);  // VALU
+      if constexpr (!E8) __builtin_amdgcn_sched_group_barrier(0x002, 4 * C::NT + 1, 0);  // VALU
       __builtin_amdgcn_sched_barrier(0);
     }
   });
   const float w6 = o.sav[6 % 4] * sb;
   const float w7 = o.sav[7 % 4] * sb;
+  [[maybe_unused]] const int ea6 = e8m0_code(o.sav[6 % 4]);
+  [[maybe_unused]] const int ea7 = e8m0_code(o.sav[7 % 4]);
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) {
-    const f32x4 p6 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[6 % 4],
-                                                                     (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-    const f32x4 p7 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[7 % 4],
-                                                                     (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+    f32x4 p6, p7;
+    if constexpr (E8) {
+      wt.acc[6][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[6 % 4], wt.acc[6][nt],
+                                                                      0, 0, 0, eb, 0, ea6);
+      wt.acc[7][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[7 % 4], wt.acc[7][nt],
+                                                                      0, 0, 0, eb, 0, ea7);
+    } else {
+      p6 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[6 % 4], (f32x4){0.f, 0.f, 0.f, 0.f},
+                                                           0, 0, 0, 0, 0, 0);
+      p7 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[7 % 4], (f32x4){0.f, 0.f, 0.f, 0.f},
+                                                           0, 0, 0, 0, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (nt == 0) {
       wait_vmcnt<IN_FLIGHT>();
@@ -463,8 +493,10 @@ __device__ __forceinline__ void step_on(WaveTile<C>& wt, Operands<C>& o, const S
       o.af[1] = frag_a<C, SN, 1>(lds);
       o.sav[1] = sa_at<C, SN, 1>(lds);
     }
-    wt.acc[6][nt] += p6 * w6;
-    wt.acc[7][nt] += p7 * w7;
+    if constexpr (!E8) {
+      wt.acc[6][nt] += p6 * w6;
+      wt.acc[7][nt] += p7 * w7;
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -508,7 +540,7 @@ __device__ __forceinline__ void zero_acc(WaveTile<C>& wt) {
 // The K loop of one tile; its first step reads stage PHASE (the global step
 // sequence runs on across tiles, so a tile with an odd number of K blocks
 // leaves the next one starting on the other stage).
-template <class C, int KIND, int PHASE>
+template <class C, int KIND, int PHASE, bool E8>
 __device__ __forceinline__ void tile_loop(const GemmArgs& p, const TileSrc& t0, const TileSrc& t1, const TileSrc& t2,
                                           WaveTile<C>& wt, int wave, int lane, const LdsOffsets& lds,
                                           const LaneOffsets& lo) {
@@ -523,13 +555,13 @@ __device__ __forceinline__ void tile_loop(const GemmArgs& p, const TileSrc& t0, 
       // The refills are issued unconditionally (past the last tile they load
       // a block nobody reads).
       const StageSrc r2 = refill_src(t0, t1, t2, kb + 2, p, k_blocks);
-      if (wt.on) step_on<C, S>(wt, op, r2, wave, lane, lds, lo);
+      if (wt.on) step_on<C, S, E8>(wt, op, r2, wave, lane, lds, lo);
       else step_off<C, S>(op, r2, wave, lane, lds, lo);
     });
   }
 }
 
-template <class C, int KIND>
+template <class C, int KIND, bool E8>
 __global__ void __launch_bounds__(C::THREADS, 1) fp8_gemm_nt_kernel(GemmArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -606,8 +638,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) fp8_gemm_nt_kernel(GemmArgs p) 
     wt.on = tile_on<C, KIND>(p, cur, cmask, wm0, wn0);
     if constexpr (KIND == KIND_CONTIGUOUS) rg = load_row_groups<C>(p, nxt, wm0, lane);
     zero_acc(wt);
-    if (phase == 0) tile_loop<C, KIND, 0>(p, c0, c1, c2, wt, wave, lane, lds, lo);
-    else tile_loop<C, KIND, 1>(p, c0, c1, c2, wt, wave, lane, lds, lo);
+    if (phase == 0) tile_loop<C, KIND, 0, E8>(p, c0, c1, c2, wt, wave, lane, lds, lo);
+    else tile_loop<C, KIND, 1, E8>(p, c0, c1, c2, wt, wave, lane, lds, lo);
     phase = (phase + k_blocks) % 2;
 
     // The next tile's row mask: its row groups were loaded when this tile
@@ -646,7 +678,7 @@ using CfgLarge = Config<256, 256, 2, 4>;
 
 template <class C, int KIND>
 static hipError_t launch(const GemmArgs& args, int num_cus, hipStream_t stream) {
-  auto kern = fp8_gemm_nt_kernel<C, KIND>;
+  auto kern = args.scale_e8m0 ? fp8_gemm_nt_kernel<C, KIND, true> : fp8_gemm_nt_kernel<C, KIND, false>;
   int per_cu = 1;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, C::THREADS, 0);
   if (e != hipSuccess) return e;

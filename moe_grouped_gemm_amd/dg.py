@@ -28,6 +28,10 @@ SIGNATURES = [
     ("dg_m_grouped_fp8_gemm_nt_contiguous", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     ("dg_m_grouped_fp8_gemm_nt_masked", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     ("dg_m_grouped_fp8_gemm_nt_nopad", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
+    ("dg_fp8_gemm_nt_ue8m0", [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp], _i),
+    ("dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
+    ("dg_m_grouped_fp8_gemm_nt_masked_ue8m0", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
+    ("dg_m_grouped_fp8_gemm_nt_nopad_ue8m0", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     ("dg_get_mk_alignment_for_contiguous_layout", [], _i),
     ("dg_get_tma_aligned_size", [_i, _i], _i),
     ("dg_get_num_cus", [], _i),
@@ -58,6 +62,11 @@ def lib() -> ctypes.CDLL:
             fn.restype = restype
         _lib = handle
     return _lib
+
+
+def _entry(name: str, ue8m0: bool):
+    """The C entry point `name`, or its power-of-two-scale variant."""
+    return getattr(lib(), name + "_ue8m0" if ue8m0 else name)
 
 
 def _check(status: int, what: str) -> None:
@@ -120,11 +129,14 @@ def get_mn_major_tma_aligned_tensor(sf: torch.Tensor) -> torch.Tensor:
 # The GEMMs
 # ---------------------------------------------------------------------------
 
-def fp8_gemm_nt(a, sfa, b, sfb, d) -> torch.Tensor:
+def fp8_gemm_nt(a, sfa, b, sfb, d, ue8m0: bool = False) -> torch.Tensor:
     """d[m, n] = bf16(sum_k a[m,k] sfa[k/128][m] * b[n,k] sfb[n/128][k/128]).
 
     a [M, K] float8_e4m3fn, sfa [K/128, tma_aligned(M)] float32,
     b [N, K] float8_e4m3fn, sfb [N/128, K/128] float32, d [M, N] bfloat16.
+    ue8m0=True calls the power-of-two-scale variant (each scale used as 2 to
+    the power of its exponent field, applied by the matrix cores); the same
+    flag exists on every GEMM below.
     """
     dev = a.device
     m, k = a.shape
@@ -140,12 +152,12 @@ def fp8_gemm_nt(a, sfa, b, sfb, d) -> torch.Tensor:
         raise ValueError("k and n must be multiples of 128")
     if tuple(sfa.shape) != (k // 128, get_tma_aligned_size(m, 4)) or tuple(sfb.shape) != (n // 128, k // 128):
         raise ValueError("scale shapes do not match the (1, 128, 128) recipe layout")
-    _check(lib().dg_fp8_gemm_nt(a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(), d.data_ptr(),
+    _check(_entry("dg_fp8_gemm_nt", ue8m0)(a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(), d.data_ptr(),
                                 m, n, k, _stream(a)), "dg_fp8_gemm_nt")
     return d
 
 
-def m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, grouped_layout) -> torch.Tensor:
+def m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, grouped_layout, ue8m0: bool = False) -> torch.Tensor:
     """Contiguous-layout grouped GEMM; grouped_layout [M] int32 holds each
     row's group (-1 for padding). b [G, N, K], sfb [G, N/128, K/128]."""
     dev = a.device
@@ -161,13 +173,13 @@ def m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, grouped_layout) -> torch
         raise ValueError("shape mismatch between a, b, d and grouped_layout")
     if tuple(sfa.shape) != (k // 128, get_tma_aligned_size(m, 4)) or tuple(sfb.shape) != (g, n // 128, k // 128):
         raise ValueError("scale shapes do not match the (1, 128, 128) recipe layout")
-    _check(lib().dg_m_grouped_fp8_gemm_nt_contiguous(
+    _check(_entry("dg_m_grouped_fp8_gemm_nt_contiguous", ue8m0)(
         a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(), d.data_ptr(), grouped_layout.data_ptr(),
         m, n, k, g, _stream(a)), "dg_m_grouped_fp8_gemm_nt_contiguous")
     return d
 
 
-def m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, d, masked_m) -> torch.Tensor:
+def m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, d, masked_m, ue8m0: bool = False) -> torch.Tensor:
     """Masked-layout grouped GEMM; masked_m [G] int32 (device) holds each
     group's valid rows. a [G, max_m, K], sfa [G, K/128, tma_aligned(max_m)],
     b [G, N, K], sfb [G, N/128, K/128], d [G, max_m, N]."""
@@ -185,13 +197,13 @@ def m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, d, masked_m) -> torch.Tensor:
     if (tuple(sfa.shape) != (g, k // 128, get_tma_aligned_size(max_m, 4))
             or tuple(sfb.shape) != (g, n // 128, k // 128)):
         raise ValueError("scale shapes do not match the (1, 128, 128) recipe layout")
-    _check(lib().dg_m_grouped_fp8_gemm_nt_masked(
+    _check(_entry("dg_m_grouped_fp8_gemm_nt_masked", ue8m0)(
         a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(), d.data_ptr(), masked_m.data_ptr(),
         g, max_m, n, k, _stream(a)), "dg_m_grouped_fp8_gemm_nt_masked")
     return d
 
 
-def m_grouped_fp8_gemm_nt_nopad(a, sfa, b, sfb, d, group_rows) -> torch.Tensor:
+def m_grouped_fp8_gemm_nt_nopad(a, sfa, b, sfb, d, group_rows, ue8m0: bool = False) -> torch.Tensor:
     """No-padding grouped GEMM; group_rows [G] int32 (device) holds each
     group's row count, the groups' rows following one another from row 0 of
     a with no alignment padding. a [M, K], sfa [K/128, tma_aligned(M)],
@@ -209,7 +221,7 @@ def m_grouped_fp8_gemm_nt_nopad(a, sfa, b, sfb, d, group_rows) -> torch.Tensor:
         raise ValueError("shape mismatch between a, b, d and group_rows")
     if tuple(sfa.shape) != (k // 128, get_tma_aligned_size(m, 4)) or tuple(sfb.shape) != (g, n // 128, k // 128):
         raise ValueError("scale shapes do not match the (1, 128, 128) recipe layout")
-    _check(lib().dg_m_grouped_fp8_gemm_nt_nopad(
+    _check(_entry("dg_m_grouped_fp8_gemm_nt_nopad", ue8m0)(
         a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(), d.data_ptr(), group_rows.data_ptr(),
         m, n, k, g, _stream(a)), "dg_m_grouped_fp8_gemm_nt_nopad")
     return d
@@ -219,12 +231,13 @@ def run_workload(w, d: torch.Tensor) -> torch.Tensor:
     """Runs the GEMM that matches a synth workload (Dense / Contiguous /
     Masked / Nopad)."""
     kind = type(w).__name__
+    e8 = getattr(w, "ue8m0", False)
     if kind == "Dense":
-        return fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d)
+        return fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d, ue8m0=e8)
     if kind == "Contiguous":
-        return m_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout)
+        return m_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout, ue8m0=e8)
     if kind == "Masked":
-        return m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m)
+        return m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m, ue8m0=e8)
     if kind == "Nopad":
-        return m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows)
+        return m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows, ue8m0=e8)
     raise TypeError(kind)

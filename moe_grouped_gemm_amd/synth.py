@@ -45,24 +45,37 @@ def tma_aligned_size(x: int, element_size: int = 4) -> int:
 # Quantisation of float32 operands (input preparation, outside the GEMM)
 # ---------------------------------------------------------------------------
 
-def quantize_lhs(x: torch.Tensor):
-    """x float32 [M, K] -> (a float8_e4m3fn [M, K], sfa float32 [K/128, tma_aligned(M)])."""
+def pow2_ceil(s: torch.Tensor) -> torch.Tensor:
+    """The smallest power of two >= s (s > 0), exactly: the UE8M0 cast of a
+    scale made at quantisation, so that x / scale stays within the E4M3 range."""
+    mant, exp = torch.frexp(s)                 # s = mant * 2^exp, mant in [0.5, 1)
+    return torch.ldexp(torch.ones_like(s), torch.where(mant == 0.5, exp - 1, exp))
+
+
+def quantize_lhs(x: torch.Tensor, ue8m0: bool = False):
+    """x float32 [M, K] -> (a float8_e4m3fn [M, K], sfa float32 [K/128, tma_aligned(M)]).
+    ue8m0: scales rounded up to powers of two before quantising."""
     m, k = x.shape
     assert k % BLOCK == 0
     xb = x.view(m, k // BLOCK, BLOCK)
     scale = xb.abs().amax(dim=-1).clamp(min=SCALE_FLOOR) / FP8_MAX       # [M, K/128]
+    if ue8m0:
+        scale = pow2_ceil(scale)
     q = (xb / scale.unsqueeze(-1)).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
     sfa = torch.zeros(k // BLOCK, tma_aligned_size(m), dtype=torch.float32, device=x.device)
     sfa[:, :m] = scale.t()
     return q.view(m, k), sfa
 
 
-def quantize_rhs(x: torch.Tensor):
-    """x float32 [N, K] -> (b float8_e4m3fn [N, K], sfb float32 [N/128, K/128])."""
+def quantize_rhs(x: torch.Tensor, ue8m0: bool = False):
+    """x float32 [N, K] -> (b float8_e4m3fn [N, K], sfb float32 [N/128, K/128]).
+    ue8m0: scales rounded up to powers of two before quantising."""
     n, k = x.shape
     assert n % BLOCK == 0 and k % BLOCK == 0
     xb = x.view(n // BLOCK, BLOCK, k // BLOCK, BLOCK)
     scale = xb.abs().amax(dim=(1, 3)).clamp(min=SCALE_FLOOR) / FP8_MAX   # [N/128, K/128]
+    if ue8m0:
+        scale = pow2_ceil(scale)
     q = (xb / scale[:, None, :, None]).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
     return q.view(n, k), scale.contiguous()
 
@@ -77,11 +90,11 @@ def _randn(shape, seed, stream, device) -> torch.Tensor:
     return torch.randn(*shape, generator=_gen(seed, stream, device), dtype=torch.float32, device=device)
 
 
-def _quantize_rhs_grouped(num_groups: int, n: int, k: int, seed: int, device):
+def _quantize_rhs_grouped(num_groups: int, n: int, k: int, seed: int, device, ue8m0: bool = False):
     b = torch.empty(num_groups, n, k, dtype=torch.float8_e4m3fn, device=device)
     sfb = torch.empty(num_groups, n // BLOCK, k // BLOCK, dtype=torch.float32, device=device)
     for g in range(num_groups):
-        bq, s = quantize_rhs(_randn((n, k), seed, 100 + g, device))
+        bq, s = quantize_rhs(_randn((n, k), seed, 100 + g, device), ue8m0)
         b[g].copy_(bq)
         sfb[g].copy_(s)
     return b, sfb
@@ -100,6 +113,7 @@ class Dense:
     m: int
     n: int
     k: int
+    ue8m0: bool = False      # power-of-two scales, for the *_ue8m0 entry points
 
     def new_output(self) -> torch.Tensor:
         return sentinel_output((self.m, self.n), self.a.device)
@@ -124,6 +138,7 @@ class Contiguous:
     n: int
     k: int
     num_groups: int
+    ue8m0: bool = False
 
     def new_output(self) -> torch.Tensor:
         return sentinel_output((self.m, self.n), self.a.device)
@@ -153,6 +168,7 @@ class Masked:
     n: int
     k: int
     num_groups: int
+    ue8m0: bool = False
 
     def new_output(self) -> torch.Tensor:
         return sentinel_output((self.num_groups, self.max_m, self.n), self.a.device)
@@ -182,6 +198,7 @@ class Nopad:
     n: int
     k: int
     num_groups: int
+    ue8m0: bool = False
 
     def new_output(self) -> torch.Tensor:
         return sentinel_output((self.m, self.n), self.a.device)
@@ -219,10 +236,10 @@ def sentinel_output(shape, device) -> torch.Tensor:
 # Generators
 # ---------------------------------------------------------------------------
 
-def make_dense(m: int, n: int, k: int, seed: int = 0, device="cpu") -> Dense:
-    a, sfa = quantize_lhs(_randn((m, k), seed, 1, device))
-    b, sfb = quantize_rhs(_randn((n, k), seed, 2, device))
-    return Dense(a, sfa, b, sfb, m, n, k)
+def make_dense(m: int, n: int, k: int, seed: int = 0, device="cpu", ue8m0: bool = False) -> Dense:
+    a, sfa = quantize_lhs(_randn((m, k), seed, 1, device), ue8m0)
+    b, sfb = quantize_rhs(_randn((n, k), seed, 2, device), ue8m0)
+    return Dense(a, sfa, b, sfb, m, n, k, ue8m0)
 
 
 def contiguous_layout(rows: List[int], align: int = BLOCK) -> np.ndarray:
@@ -238,49 +255,49 @@ def contiguous_layout(rows: List[int], align: int = BLOCK) -> np.ndarray:
 
 
 def make_contiguous(rows: List[int], n: int, k: int, seed: int = 0, device="cpu",
-                    poison_padding: bool = False) -> Contiguous:
+                    poison_padding: bool = False, ue8m0: bool = False) -> Contiguous:
     layout_np = contiguous_layout(rows)
     m = int(layout_np.size)
-    a, sfa = quantize_lhs(_randn((max(m, 1), k), seed, 1, device))
+    a, sfa = quantize_lhs(_randn((max(m, 1), k), seed, 1, device), ue8m0)
     a = a[:m].contiguous()
     sfa = sfa[:, :tma_aligned_size(m)].contiguous() if m else torch.zeros(k // BLOCK, 0, device=device)
     layout = torch.from_numpy(layout_np).to(device)
     if poison_padding and m:
         pad = layout < 0
         a.view(torch.uint8)[pad] = 0x7F  # E4M3 NaN
-    b, sfb = _quantize_rhs_grouped(len(rows), n, k, seed, device)
-    return Contiguous(a, sfa, b, sfb, layout, list(map(int, rows)), m, n, k, len(rows))
+    b, sfb = _quantize_rhs_grouped(len(rows), n, k, seed, device, ue8m0)
+    return Contiguous(a, sfa, b, sfb, layout, list(map(int, rows)), m, n, k, len(rows), ue8m0)
 
 
 def make_masked(counts: List[int], max_m: int, n: int, k: int, seed: int = 0, device="cpu",
-                poison_invalid: bool = False) -> Masked:
+                poison_invalid: bool = False, ue8m0: bool = False) -> Masked:
     num_groups = len(counts)
     a = torch.empty(num_groups, max_m, k, dtype=torch.float8_e4m3fn, device=device)
     sfa = torch.zeros(num_groups, k // BLOCK, tma_aligned_size(max_m), dtype=torch.float32, device=device)
     for g in range(num_groups):
-        aq, s = quantize_lhs(_randn((max_m, k), seed, 1000 + g, device))
+        aq, s = quantize_lhs(_randn((max_m, k), seed, 1000 + g, device), ue8m0)
         a[g].copy_(aq)
         sfa[g].copy_(s)
         if poison_invalid:
             valid = min(max(int(counts[g]), 0), max_m)
             a[g, valid:].view(torch.uint8).fill_(0x7F)
-    b, sfb = _quantize_rhs_grouped(num_groups, n, k, seed, device)
+    b, sfb = _quantize_rhs_grouped(num_groups, n, k, seed, device, ue8m0)
     masked_m = torch.tensor(list(counts), dtype=torch.int32, device=device)
-    return Masked(a, sfa, b, sfb, masked_m, list(map(int, counts)), max_m, n, k, num_groups)
+    return Masked(a, sfa, b, sfb, masked_m, list(map(int, counts)), max_m, n, k, num_groups, ue8m0)
 
 
 def make_nopad(rows: List[int], n: int, k: int, seed: int = 0, device="cpu", tail: int = 0,
-               m: Optional[int] = None, poison_tail: bool = False) -> Nopad:
+               m: Optional[int] = None, poison_tail: bool = False, ue8m0: bool = False) -> Nopad:
     """Groups' rows back to back with no padding, then `tail` rows that no
     group owns (or exactly m rows when m is given)."""
     if m is None:
         m = int(sum(max(int(r), 0) for r in rows)) + tail
-    a, sfa = quantize_lhs(_randn((max(m, 1), k), seed, 1, device))
+    a, sfa = quantize_lhs(_randn((max(m, 1), k), seed, 1, device), ue8m0)
     a = a[:m].contiguous()
     sfa = sfa[:, :tma_aligned_size(m)].contiguous() if m else torch.zeros(k // BLOCK, 0, device=device)
-    b, sfb = _quantize_rhs_grouped(len(rows), n, k, seed, device)
+    b, sfb = _quantize_rhs_grouped(len(rows), n, k, seed, device, ue8m0)
     group_rows = torch.tensor(list(rows), dtype=torch.int32, device=device)
-    w = Nopad(a, sfa, b, sfb, group_rows, list(map(int, rows)), m, n, k, len(rows))
+    w = Nopad(a, sfa, b, sfb, group_rows, list(map(int, rows)), m, n, k, len(rows), ue8m0)
     if poison_tail and m:
         used = max([e for _, e in w.row_ranges()], default=0)
         a.view(torch.uint8)[used:] = 0x7F  # E4M3 NaN
@@ -324,7 +341,9 @@ def workload_spec(index: int, seed: int = 0) -> WorkloadSpec:
     2 contiguous, 8 groups with rows uniform in [3000, 5000], N=4096, K=7168;
     3 masked decode, 16 groups, max_m=256, masked_m uniform in [1, 256], N=7168, K=2048;
     4 contiguous, 32 groups with Zipf(1.2) rows totalling 65536, N=4096, K=7168;
-    5 no-padding layout of workload 2's groups (the same row counts, not padded).
+    5 no-padding layout of workload 2's groups (the same row counts, not padded);
+    6, 7, 8: workloads 1, 2 and 3 with power-of-two (UE8M0-cast) scales, for
+    the *_ue8m0 entry points.
     """
     if index == 0:
         return WorkloadSpec(0, "dense", "dense_128x256x512", n=256, k=512, m=128)
@@ -342,21 +361,26 @@ def workload_spec(index: int, seed: int = 0) -> WorkloadSpec:
     if index == 5:
         rows = [int(x) for x in _structure_rng(seed).integers(3000, 5001, size=8)]
         return WorkloadSpec(5, "nopad", "nopad_8x[3000,5000]_n4096_k7168", n=4096, k=7168, rows=rows)
+    if index in (6, 7, 8):
+        base = workload_spec(index - 5, seed)
+        return WorkloadSpec(index, base.kind, base.name + "_ue8m0", n=base.n, k=base.k, m=base.m, rows=base.rows,
+                            counts=base.counts, max_m=base.max_m, extra={"ue8m0": True})
     raise ValueError(f"no workload {index}")
 
 
-NUM_WORKLOADS = 6
+NUM_WORKLOADS = 9
 
 
 def make_workload(spec: WorkloadSpec, seed: int = 0, device="cpu"):
+    e8 = bool(spec.extra.get("ue8m0", False))
     if spec.kind == "dense":
-        return make_dense(spec.m, spec.n, spec.k, seed, device)
+        return make_dense(spec.m, spec.n, spec.k, seed, device, ue8m0=e8)
     if spec.kind == "contiguous":
-        return make_contiguous(spec.rows, spec.n, spec.k, seed, device)
+        return make_contiguous(spec.rows, spec.n, spec.k, seed, device, ue8m0=e8)
     if spec.kind == "masked":
-        return make_masked(spec.counts, spec.max_m, spec.n, spec.k, seed, device)
+        return make_masked(spec.counts, spec.max_m, spec.n, spec.k, seed, device, ue8m0=e8)
     if spec.kind == "nopad":
-        return make_nopad(spec.rows, spec.n, spec.k, seed, device)
+        return make_nopad(spec.rows, spec.n, spec.k, seed, device, ue8m0=e8)
     raise ValueError(spec.kind)
 
 

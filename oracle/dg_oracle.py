@@ -29,7 +29,8 @@ Sources on the pages:
     counts says where each group's rows are.
   * "DeepGEMM Compatibility Wrapper (deep-gemm)" page, "0.2.7 Compatibility
     Additions" and "Contiguous Grouped GEMM Alignment": scale recipe
-    (1, 128, 128) and the 128-row segment alignment.
+    (1, 128, 128) and the 128-row segment alignment; UE8M0 scale casting and
+    the packed UE8M0 scale conversion (the *_ue8m0 variants below).
 
 The 128-K block structure of the scales does not change the definition: the
 per-block sums scaled and added are algebraically the plain sum over the
@@ -49,6 +50,11 @@ design notes of the repository):
     D. A negative count counts as zero; rows at or past M do not exist, so a
     group reaching past them is cut off there. Rows no group owns are left
     untouched.
+  * UE8M0 variants: the scales are powers of two (a UE8M0 cast made at
+    quantisation); a float32 scale is taken as 2^(e - 127), e being its
+    biased exponent field, as the packed UE8M0 conversion reads it (sign and
+    mantissa bits dropped; e = 255 is NaN). The GEMM is then the same
+    definition with those scale values.
 """
 
 from __future__ import annotations
@@ -74,6 +80,11 @@ __all__ = [
     "contiguous_f64_at",
     "masked_f64_at",
     "nopad_f64_at",
+    "e8m0_value",
+    "fp8_gemm_nt_ue8m0",
+    "m_grouped_fp8_gemm_nt_contiguous_ue8m0",
+    "m_grouped_fp8_gemm_nt_masked_ue8m0",
+    "m_grouped_fp8_gemm_nt_nopad_ue8m0",
 ]
 
 # Scale granularity along K for both operands: recipe (1, 128, 128).
@@ -341,3 +352,36 @@ def nopad_f64_at(a_codes, sfa, b_codes, sfb, group_rows, rows, cols) -> np.ndarr
         if sel.size:
             out[sel] = _rows_cols_f64(a_codes, sfa, b_codes[g], sfb[g], rows[sel], cols)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Power-of-two (UE8M0) scales
+# ---------------------------------------------------------------------------
+
+def e8m0_value(scales) -> np.ndarray:
+    """float64 value of each float32 scale read as an E8M0 code: the biased
+    exponent field e (bits 30..23 of the float32 encoding) stands for
+    2^(e - 127), and e = 255 for NaN (OCP Microscaling formats, E8M0). For a
+    positive normal power of two this is the scale itself."""
+    bits = np.ascontiguousarray(scales, dtype=np.float32).view(np.uint32)
+    e = ((bits >> 23) & 0xFF).astype(np.int64)
+    out = np.ldexp(1.0, e - 127)
+    out[e == 255] = np.nan
+    return out
+
+
+def fp8_gemm_nt_ue8m0(a_codes, sfa, b_codes, sfb, d_init=None) -> np.ndarray:
+    """Dense GEMM with every scale taken as its E8M0 value."""
+    return fp8_gemm_nt(a_codes, e8m0_value(sfa), b_codes, e8m0_value(sfb), d_init)
+
+
+def m_grouped_fp8_gemm_nt_contiguous_ue8m0(a_codes, sfa, b_codes, sfb, layout, d_init) -> np.ndarray:
+    return m_grouped_fp8_gemm_nt_contiguous(a_codes, e8m0_value(sfa), b_codes, e8m0_value(sfb), layout, d_init)
+
+
+def m_grouped_fp8_gemm_nt_masked_ue8m0(a_codes, sfa, b_codes, sfb, masked_m, d_init) -> np.ndarray:
+    return m_grouped_fp8_gemm_nt_masked(a_codes, e8m0_value(sfa), b_codes, e8m0_value(sfb), masked_m, d_init)
+
+
+def m_grouped_fp8_gemm_nt_nopad_ue8m0(a_codes, sfa, b_codes, sfb, group_rows, d_init) -> np.ndarray:
+    return m_grouped_fp8_gemm_nt_nopad(a_codes, e8m0_value(sfa), b_codes, e8m0_value(sfb), group_rows, d_init)

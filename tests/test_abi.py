@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = dg.lib()
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 13, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(n for n, _, _ in dg.SIGNATURES) == names
@@ -122,6 +122,24 @@ def test_nopad_shapes():
 def test_alignment(call):
     for arg, val in (("a", A + 8), ("b", B + 4), ("d", D + 2), ("sfa", SFA + 4), ("sfb", SFB + 8)):
         assert call(**{arg: val}) == 3
+
+
+def test_ue8m0_variants_share_the_checks():
+    lib = dg.lib()
+    calls = {
+        "dense": lambda **kw: lib.dg_fp8_gemm_nt_ue8m0(kw.get("a", A), SFA, B, SFB, D, 256, kw.get("n", 256), 512,
+                                                        None),
+        "contiguous": lambda **kw: lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(
+            kw.get("a", A), SFA, B, SFB, D, AUX, 256, kw.get("n", 256), 512, 2, None),
+        "masked": lambda **kw: lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0(
+            kw.get("a", A), SFA, B, SFB, D, AUX, 2, 64, kw.get("n", 256), 512, None),
+        "nopad": lambda **kw: lib.dg_m_grouped_fp8_gemm_nt_nopad_ue8m0(
+            kw.get("a", A), SFA, B, SFB, D, AUX, 256, kw.get("n", 256), 512, 2, None),
+    }
+    for name, call in calls.items():
+        assert call(a=None) == 1, name
+        assert call(a=A + 8) == 3, name
+        assert call(n=192) == 2, name
 
 
 def test_no_device_reported_without_gpu():

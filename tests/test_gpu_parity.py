@@ -367,6 +367,94 @@ def test_nopad_graph_replay_follows_device_counts(dev):
 
 
 # ---------------------------------------------------------------------------
+# Power-of-two (UE8M0) scales: the *_ue8m0 entry points
+# ---------------------------------------------------------------------------
+
+def _assert_pow2(*scales):
+    for s in scales:
+        s = NP(s)
+        s = s[s != 0]   # the zero padding of the aligned LHS-scale rows is never read
+        assert np.array_equal(O.e8m0_value(s), s.astype(np.float64)), "scales are not powers of two"
+
+
+@pytest.mark.parametrize("m,n,k", [(128, 256, 512), (300, 384, 1024), (1, 896, 128), (257, 1792, 8192)])
+def test_ue8m0_dense(dev, m, n, k):
+    _say(f"ue8m0 dense {m}x{n}x{k}")
+    w = synth.make_dense(m, n, k, seed=m + k, device=dev, ue8m0=True)
+    _assert_pow2(w.sfa, w.sfb)
+    d = w.new_output()
+    dg.fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d, ue8m0=True)
+    torch.cuda.synchronize()
+    ref = O.gemm_nt_f64(NP(w.a), O.e8m0_value(NP(w.sfa)), NP(w.b), O.e8m0_value(NP(w.sfb)))
+    check_close(NP(d), ref, f"ue8m0 dense {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(200, 256, 1024), (77, 896, 512), (65, 256, 4096)])
+def test_ue8m0_integer_exact_bitwise(dev, m, n, k):
+    _say(f"ue8m0 integer-exact {m}x{n}x{k}")
+    a, sfa, b, sfb = _int_exact(m, n, k, seed=m + 1)
+    d = synth.sentinel_output((m, n), dev)
+    dg.fp8_gemm_nt(_dev_fp8(a, dev), torch.from_numpy(sfa).to(dev), _dev_fp8(b, dev),
+                   torch.from_numpy(sfb).to(dev), d, ue8m0=True)
+    torch.cuda.synchronize()
+    ref_bits = O.fp8_gemm_nt_ue8m0(a, sfa, b, sfb)
+    got = NP(d)
+    assert np.array_equal(got, ref_bits), f"{np.sum(got != ref_bits)} mismatching elements"
+
+
+@pytest.mark.parametrize("k", [512, 4096])
+def test_ue8m0_grouped_layouts(dev, k):
+    _say(f"ue8m0 grouped layouts k={k}")
+    rows = [130, 0, 77, 256, 1]
+    w = synth.make_contiguous(rows, 256, k, seed=21, device=dev, poison_padding=True, ue8m0=True)
+    _assert_pow2(w.sfa, w.sfb)
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout, ue8m0=True)
+    torch.cuda.synchronize()
+    _check_contiguous(w, d, "ue8m0 contiguous")
+    counts = [0, 1, 200, 77]
+    w = synth.make_masked(counts, 200, 256, k, seed=22, device=dev, poison_invalid=True, ue8m0=True)
+    _assert_pow2(w.sfa, w.sfb)
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m, ue8m0=True)
+    torch.cuda.synchronize()
+    _check_masked(w, d, counts, "ue8m0 masked")
+    w = synth.make_nopad(rows, 256, k, seed=23, device=dev, tail=7, poison_tail=True, ue8m0=True)
+    _assert_pow2(w.sfa, w.sfb)
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows, ue8m0=True)
+    torch.cuda.synchronize()
+    _check_nopad(w, d, "ue8m0 nopad")
+
+
+def test_ue8m0_drops_mantissa(dev):
+    """Scales that are not powers of two: the mantissa bits are ignored, so the
+    output equals the call on the scales rounded down to powers of two, bit
+    for bit, and the oracle's UE8M0 variant within the tolerance."""
+    w = synth.make_dense(256, 512, 1024, seed=3, device=dev)   # amax/448 scales
+    floor_sfa = torch.from_numpy(O.e8m0_value(NP(w.sfa)).astype(np.float32)).to(dev)
+    floor_sfb = torch.from_numpy(O.e8m0_value(NP(w.sfb)).astype(np.float32)).to(dev)
+    d1, d2 = w.new_output(), w.new_output()
+    dg.fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d1, ue8m0=True)
+    dg.fp8_gemm_nt(w.a, floor_sfa, w.b, floor_sfb, d2, ue8m0=True)
+    torch.cuda.synchronize()
+    assert torch.equal(d1.view(torch.int16), d2.view(torch.int16))
+    ref = O.gemm_nt_f64(NP(w.a), O.e8m0_value(NP(w.sfa)), NP(w.b), O.e8m0_value(NP(w.sfb)))
+    check_close(NP(d1), ref, "ue8m0 mantissa dropped")
+
+
+def test_ue8m0_close_to_float32_path(dev):
+    """On power-of-two scales both paths compute the same sum (float32
+    accumulation, different order): they agree within the tolerance."""
+    w = synth.make_dense(512, 1024, 2048, seed=4, device=dev, ue8m0=True)
+    d1, d2 = w.new_output(), w.new_output()
+    dg.fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d1, ue8m0=True)
+    dg.fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d2)
+    torch.cuda.synchronize()
+    check_close(NP(d1), O.bf16_bits_to_f64(NP(d2)), "ue8m0 vs float32 scales")
+
+
+# ---------------------------------------------------------------------------
 # The benchmark workloads at full size (sampled comparison)
 # ---------------------------------------------------------------------------
 
@@ -387,6 +475,8 @@ def test_workload_full_size(dev, index):
     rng = np.random.default_rng(100 + index)
     got = NP(d)
     a, sfa, b, sfb = NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb)
+    if w.ue8m0:
+        sfa, sfb = O.e8m0_value(sfa), O.e8m0_value(sfb)
     if spec.kind == "dense":
         rows = _sample(w.m, 96, rng, (0, 127, 128, 255, 256, w.m - 1))
         cols = _sample(w.n, 96, rng, (0, 127, 128, 255, w.n - 1))

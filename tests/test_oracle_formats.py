@@ -87,6 +87,23 @@ def test_bf16_golden_cases():
     check_bf16_golden(O)
 
 
+def check_e8m0_golden(orc):
+    rows = _read_golden("e8m0_scale_cases.txt")
+    assert len(rows) >= 12
+    for row in rows:
+        bits_s, val_s = row.split("#")[0].split()
+        bits = np.array([int(bits_s, 16)], dtype=np.uint32)
+        got = orc.e8m0_value(bits.view(np.float32))[0]
+        if val_s == "nan":
+            assert math.isnan(got), bits_s
+        else:
+            assert got == float(eval(val_s, {"__builtins__": {}}, {})), (bits_s, got)
+
+
+def test_e8m0_golden_cases():
+    check_e8m0_golden(O)
+
+
 def test_bf16_single_rounding_from_f64():
     # 1 + 2^-8 + 2^-40 is just above a tie; rounding through float32 first would
     # land exactly on the tie and then go down to 1.0

@@ -11,7 +11,10 @@ Each pin checks the oracle against something other than its own code:
   * invariants: grouped == per-group dense, permuting segments permutes rows,
     masked and padding rows untouched, NaN-poisoned padding does not leak,
     the no-padding layout with 128-aligned counts == the contiguous layout;
-  * a no-padding row owner map built by walking the counts row by row.
+  * a no-padding row owner map built by walking the counts row by row;
+  * UE8M0 scales: a hand-derived table of float32 bit patterns and their
+    E8M0 values (tests/golden/e8m0_scale_cases.txt), the float32 variants on
+    power-of-two scales, and math.frexp rounding down for other scales.
 
 test_planted_mistakes_are_caught plants plausible mistakes in a private copy
 of the oracle (wrong scale index, transposed RHS scales, wrong FP8 flavour,
@@ -335,6 +338,51 @@ def pin_nopad_layout_invariants(orc):
     assert not np.any(np.isnan(O.bf16_bits_to_f64(d[:7])))
 
 
+def _pow2_inputs(rng, m, n, k, groups=None):
+    a, sfa, b, sfb = _random_inputs(rng, m, n, k, groups)
+    return (a, np.ldexp(1.0, rng.integers(-8, 3, size=sfa.shape)).astype(np.float32), b,
+            np.ldexp(1.0, rng.integers(-8, 3, size=sfb.shape)).astype(np.float32))
+
+
+def pin_ue8m0_power_of_two_identity(orc):
+    """With scales that are powers of two the UE8M0 variants are the float32
+    variants, bit for bit, for every layout."""
+    rng = np.random.default_rng(41)
+    a, sfa, b, sfb = _pow2_inputs(rng, 40, 256, 384)
+    assert np.array_equal(orc.fp8_gemm_nt_ue8m0(a, sfa, b, sfb), orc.fp8_gemm_nt(a, sfa, b, sfb))
+    a, sfa, b, sfb = _pow2_inputs(rng, 256, 128, 256, groups=2)
+    d0 = np.full((256, 128), 0xFFFF, np.uint16)
+    layout = np.r_[np.zeros(100), np.full(28, -1), np.ones(128)].astype(np.int32)
+    assert np.array_equal(orc.m_grouped_fp8_gemm_nt_contiguous_ue8m0(a, sfa, b, sfb, layout, d0),
+                          orc.m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, layout, d0))
+    counts = np.array([100, 120], np.int32)
+    assert np.array_equal(orc.m_grouped_fp8_gemm_nt_nopad_ue8m0(a, sfa, b, sfb, counts, d0),
+                          orc.m_grouped_fp8_gemm_nt_nopad(a, sfa, b, sfb, counts, d0))
+    am = a.reshape(2, 128, 256)
+    sfam = np.stack([sfa[:, :128], sfa[:, 128:]])
+    d0m = np.full((2, 128, 128), 0xFFFF, np.uint16)
+    assert np.array_equal(orc.m_grouped_fp8_gemm_nt_masked_ue8m0(am, sfam, b, sfb, counts, d0m),
+                          orc.m_grouped_fp8_gemm_nt_masked(am, sfam, b, sfb, counts, d0m))
+
+
+def pin_ue8m0_drops_mantissa(orc):
+    """Arbitrary positive scales: the UE8M0 variant equals the float32 one on
+    scales rounded down to powers of two (math.frexp: s = f * 2^e, f in
+    [0.5, 1), so the power of two at or below s is 2^(e - 1))."""
+    rng = np.random.default_rng(43)
+    a, sfa, b, sfb = _random_inputs(rng, 24, 256, 384)
+
+    def floor_pow2(x):
+        return np.vectorize(lambda v: math.ldexp(1.0, math.frexp(float(v))[1] - 1))(x).astype(np.float32)
+    assert np.array_equal(orc.fp8_gemm_nt_ue8m0(a, sfa, b, sfb),
+                          orc.fp8_gemm_nt(a, floor_pow2(sfa), b, floor_pow2(sfb)))
+
+
+def pin_e8m0_golden(orc):
+    import test_oracle_formats as F
+    F.check_e8m0_golden(orc)
+
+
 def pin_contiguous_poisoned_padding(orc):
     rng = np.random.default_rng(17)
     rows = [5, 128, 1]
@@ -398,6 +446,9 @@ PINS = [
     pin_sampled_matches_full,
     pin_exact_nopad,
     pin_nopad_layout_invariants,
+    pin_e8m0_golden,
+    pin_ue8m0_power_of_two_identity,
+    pin_ue8m0_drops_mantissa,
 ]
 
 
@@ -544,6 +595,28 @@ def _mut_nopad_last_group_to_end(mod):
     mod.nopad_row_ranges = f
 
 
+def _mut_e8m0_rounds_up(mod):
+    # the next power of two at or above the scale instead of its exponent field
+    def f(scales):
+        x = np.asarray(scales, np.float64)
+        return np.ldexp(1.0, np.ceil(np.log2(np.abs(x))).astype(np.int64))
+    mod.e8m0_value = f
+
+
+def _mut_e8m0_bias_128(mod):
+    orig = mod.e8m0_value
+
+    def f(scales):
+        return orig(scales) / 2.0
+    mod.e8m0_value = f
+
+
+def _mut_e8m0_keeps_mantissa(mod):
+    def f(scales):
+        return np.asarray(scales, np.float64)
+    mod.e8m0_value = f
+
+
 MUTANTS = [
     _mut_lhs_scale_first_row,
     _mut_rhs_scale_transposed,
@@ -558,6 +631,9 @@ MUTANTS = [
     _mut_nopad_groups_restart,
     _mut_nopad_negative_counts,
     _mut_nopad_last_group_to_end,
+    _mut_e8m0_rounds_up,
+    _mut_e8m0_bias_128,
+    _mut_e8m0_keeps_mantissa,
 ]
 
 
