@@ -41,7 +41,8 @@
  * the only library state is the CU-count setting.
  *
  * Limits: K <= 2^20, N <= 2^20, every operand < 2^40 bytes, num_groups <= 4096
- * for the masked layout and <= 2048 for the no-padding layout.
+ * for the masked layout, <= 2048 for the no-padding layout and <= 512 for
+ * the K-grouped GEMM.
  */
 #ifndef DG_H
 #define DG_H
@@ -172,6 +173,34 @@ dg_status dg_m_grouped_fp8_gemm_nt_nopad_ue8m0(const void* a, const float* sfa,
                                                void* d, const int32_t* group_rows,
                                                int m, int n, int k, int num_groups,
                                                void* stream);
+
+/*
+ * K-grouped FP8 NT GEMM, contiguous K groups: the weight-gradient shape of
+ * an MoE layer ("DeepGEMM Compatibility Wrapper" page, "0.2.7 Compatibility
+ * Additions": K sizes given on the host, each a multiple of 128, scale recipe
+ * (1, 1, 128); per the wrapper's notes, a missing C means D starts from
+ * zero, a separate C is the starting value of D, and C given as D itself
+ * accumulates into D).
+ *   ks  [num_groups] int (HOST memory): K of each group, each >= 0 and a
+ *       multiple of 128; K = sum of ks; group g owns K positions
+ *       [sum_{j<g} ks[j], sum_{j<=g} ks[j]).
+ *   a   [m][K] E4M3                     sfa [K/128][dg_get_tma_aligned_size(m,4)] float32
+ *   b   [n][K] E4M3                     sfb [K/128][dg_get_tma_aligned_size(n,4)] float32
+ *       (one scale per row and 128-wide K block for both operands)
+ *   c   [num_groups][m][n] float32 or NULL; d [num_groups][m][n] float32
+ *   d[g][i][j] = (c ? c[g][i][j] : 0)
+ *                + sum_{k in group g} e4m3(a[i][k]) sfa[k/128][i] * e4m3(b[j][k]) sfb[k/128][j]
+ * c may equal d (accumulation in place); otherwise c and d must not
+ * overlap. A group with ks = 0 gets d[g] = c[g] (or zeros). Products
+ * accumulate in float32 with a promotion per 128-K block, as for the other
+ * GEMMs. num_groups in [1, 512] (an empty ks is rejected), m >= 0 (m == 0 is
+ * a no-op), n % 128 == 0, K <= 2^20; c (when given) 16-byte aligned.
+ */
+dg_status dg_k_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa,
+                                              const void* b, const float* sfb,
+                                              const float* c, float* d,
+                                              const int* ks, int num_groups,
+                                              int m, int n, void* stream);
 
 /* Row alignment of each group's segment in the contiguous layout: 128
  * ("DeepGEMM Compatibility Wrapper" page, "Contiguous Grouped GEMM

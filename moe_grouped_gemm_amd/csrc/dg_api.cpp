@@ -202,6 +202,51 @@ dg_status dg_m_grouped_fp8_gemm_nt_nopad_ue8m0(const void* a, const float* sfa, 
   return nopad(a, sfa, b, sfb, d, group_rows, m, n, k, num_groups, true, stream);
 }
 
+dg_status dg_k_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, const void* b, const float* sfb,
+                                              const float* c, float* d, const int* ks, int num_groups, int m, int n,
+                                              void* stream) {
+  if (!a || !sfa || !b || !sfb || !d || !ks) return DG_ERR_NULL;
+  if (num_groups <= 0 || m < 0 || n <= 0 || n % 128 != 0) return DG_ERR_SHAPE;
+  if (num_groups > dg::MAX_KGROUPED_GROUPS) return DG_ERR_UNSUPPORTED;
+  if (n > kMaxDim) return DG_ERR_UNSUPPORTED;
+  long long k = 0;
+  for (int g = 0; g < num_groups; ++g) {
+    if (ks[g] < 0 || ks[g] % 128 != 0) return DG_ERR_SHAPE;
+    k += ks[g];
+    if (k > kMaxDim) return DG_ERR_UNSUPPORTED;
+  }
+  if ((long long)m * k >= kMaxBytes || (long long)n * k >= kMaxBytes ||
+      (long long)num_groups * m * n * 4 >= kMaxBytes)
+    return DG_ERR_UNSUPPORTED;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(d) || !aligned16(sfa) || !aligned16(sfb) ||
+      (c && !aligned16(c)))
+    return DG_ERR_ALIGN;
+  if (m == 0) return DG_OK;
+  dg::KGroupedArgs args{};
+  args.a = static_cast<const uint8_t*>(a);
+  args.sfa = sfa;
+  args.b = static_cast<const uint8_t*>(b);
+  args.sfb = sfb;
+  args.c = c;
+  args.d = d;
+  args.m = m;
+  args.n = n;
+  args.k = (int)k;
+  args.num_groups = num_groups;
+  args.ld_sfa = tma_aligned(m, 4);
+  args.ld_sfb = tma_aligned(n, 4);
+  int off = 0;
+  for (int g = 0; g < num_groups; ++g) {
+    args.k_off[g] = off;
+    off += ks[g] / 128;
+  }
+  args.k_off[num_groups] = off;
+  const int cus = effective_cus();
+  if (cus <= 0) return DG_ERR_DEVICE;
+  return dg::launch_k_grouped(args, cus, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? DG_OK
+                                                                                                : DG_ERR_LAUNCH;
+}
+
 int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }
 
 int dg_get_tma_aligned_size(int x, int element_size) {

@@ -37,6 +37,27 @@ struct GemmArgs {
   int m_blocks, n_blocks, num_tiles;  // filled in by launch_gemm
 };
 
+// Largest group count of the K-grouped GEMM (its group offsets travel in the
+// kernel arguments).
+constexpr int MAX_KGROUPED_GROUPS = 512;
+
+// Arguments of the K-grouped GEMM (dg_kernel_kgrouped.hip), passed by value.
+struct KGroupedArgs {
+  const uint8_t* a;    // [m][k] E4M3
+  const float* sfa;    // [k/128][ld_sfa]
+  const uint8_t* b;    // [n][k] E4M3
+  const float* sfb;    // [k/128][ld_sfb]
+  const float* c;      // [G][m][n] or null (then D is the product alone); may equal d
+  float* d;            // [G][m][n]
+  int m, n, k;         // k: the total K, also the row stride of A and B
+  int num_groups;
+  int ld_sfa, ld_sfb;
+  int m_blocks, n_blocks, num_tiles;       // filled in by launch_k_grouped
+  int k_off[MAX_KGROUPED_GROUPS + 1];      // first K block of each group; k_off[G] = k / 128
+};
+
+hipError_t launch_k_grouped(KGroupedArgs& args, int num_cus, hipStream_t stream);
+
 // Enqueues the kernel for `kind` on `stream`; arguments already validated.
 hipError_t launch_gemm(int kind, GemmArgs args, int num_cus, hipStream_t stream);
 

@@ -1,0 +1,226 @@
+// K-grouped FP8 (OCP E4M3) NT GEMM for gfx950 (MI355X): the weight-gradient
+// shape of an MoE layer ("DeepGEMM Compatibility Wrapper" page, "0.2.7
+// Compatibility Additions": contiguous K-grouped FP8 NT GEMM with host-side
+// K sizes, each a multiple of 128, scale recipe (1, 1, 128), and a float32
+// C that is cleared, copied or accumulated in place).
+//
+// The K axis is split into consecutive groups; group g owns K blocks
+// [k_off[g], k_off[g + 1]) of A [M][K] and B [N][K] (row stride K) and has
+// its own float32 output D[g] [M][N]:
+//
+//   D[g][m][n] = C[g][m][n] + sum over k in group g of
+//                e4m3(A[m][k]) sfa[k/128][m] * e4m3(B[n][k]) sfb[k/128][n]
+//
+// Both operands carry one float32 scale per row and 128-wide K block, stored
+// transposed (sfa [K/128][align4(M)], sfb [K/128][align4(N)]).
+//
+// One persistent kernel walks all groups' 256 x 256 output tiles, group by
+// group. Per tile it runs a double-buffered K loop over the group's blocks:
+// the direct-to-LDS 16-byte buffer loads of block i + 1 are issued right
+// after the barrier that frees their stage, then block i is multiplied (one
+// v_mfma_f32_16x16x128_f8f6f4 per 16x16 sub-tile, the B fragment as the
+// first operand, so a lane's four results share one row and cover four
+// consecutive columns) and promoted: total += partial * (sfa[m] * sfb[n]),
+// where the RHS scale now differs per column. The float32 totals, plus C,
+// are stored 16 bytes per lane.
+
+#include "dg_device.h"
+
+namespace dg {
+namespace kgrouped {
+
+constexpr int BM = 256, BN = 256, WAVES_N = 4, NW = 8, THREADS = NW * 64;
+constexpr int WM = 128, WN = 64, MT = WM / 16, NT = WN / 16;
+constexpr int A_BYTES = BM * ROW_BYTES, B_BYTES = BN * ROW_BYTES;
+constexpr int SA_OFF = A_BYTES + B_BYTES;  // the tile rows' LHS scales (float32)
+constexpr int SB_OFF = SA_OFF + BM * 4;    // the tile columns' RHS scales (float32)
+constexpr int STAGE_BYTES = SB_OFF + BN * 4;
+constexpr int AB_LOADS = BM * ROW_BYTES / 1024 / NW;  // wave-wide 16-byte loads per operand and wave
+static_assert(AB_LOADS == 4 && BM / NW * 2 == 64, "load split");
+
+__device__ __forceinline__ uint8_t* lds() {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[2 * STAGE_BYTES];
+  return buf;
+}
+
+__device__ __forceinline__ uint32_t lds_addr() { return (uint32_t)(uintptr_t)(lds_void*)lds(); }
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_dest(lds_base), 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_dest(lds_base), 4, voff, 0, 0, 0);
+}
+
+// One output tile: its group, origin, K blocks and real rows / columns.
+struct Tile {
+  int g, m0, n0, kb0, nkb;
+  int a_rows, b_rows;
+};
+
+__device__ __forceinline__ Tile tile_at(const KGroupedArgs& p, int t) {
+  Tile tl;
+  const int per_group = p.m_blocks * p.n_blocks;
+  tl.g = t / per_group;
+  int mb, nb;
+  raster(t - tl.g * per_group, p.m_blocks, p.n_blocks, 8, mb, nb);
+  tl.m0 = mb * BM;
+  tl.n0 = nb * BN;
+  tl.kb0 = p.k_off[tl.g];
+  tl.nkb = p.k_off[tl.g + 1] - tl.kb0;
+  tl.a_rows = min(BM, p.m - tl.m0);
+  tl.b_rows = min(BN, p.n - tl.n0);
+  return tl;
+}
+
+// Issues the loads of K block kb of a tile into the stage at LDS byte
+// address `st`. Wave w loads rows w * 8 + lane / 8 + 64 j (j < 4) of the A
+// and the B tile, 16 bytes each and chunk-swizzled as lds_offset() reads
+// them (lane_off is row * K + 16 * chunk); waves 0-3 also load 64 of the
+// tile's LHS scales each, waves 4-7 64 of its RHS scales. Rows and columns
+// past the matrix read as zero.
+__device__ __forceinline__ void issue_block(const KGroupedArgs& p, const Tile& tl, int kb, uint32_t st, int wave,
+                                            int lane, uint32_t lane_off) {
+  const uint32_t lda = (uint32_t)p.k;
+  const __amdgpu_buffer_rsrc_t ra =
+      buffer_rsrc(p.a + (size_t)tl.m0 * lda + (size_t)kb * BK, (uint32_t)tl.a_rows * lda);
+  const __amdgpu_buffer_rsrc_t rb =
+      buffer_rsrc(p.b + (size_t)tl.n0 * lda + (size_t)kb * BK, (uint32_t)tl.b_rows * lda);
+#pragma unroll
+  for (int j = 0; j < AB_LOADS; ++j) {
+    dma16(ra, lane_off + (uint32_t)j * 64u * lda, st + (j * NW + wave) * 1024);
+    dma16(rb, lane_off + (uint32_t)j * 64u * lda, st + A_BYTES + (j * NW + wave) * 1024);
+  }
+  if (wave < 4) {
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(p.sfa + (size_t)kb * p.ld_sfa + tl.m0, (uint32_t)tl.a_rows * 4u);
+    dma4(rs, (uint32_t)(wave * 64 + lane) * 4u, st + SA_OFF + wave * 256);
+  } else {
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(p.sfb + (size_t)kb * p.ld_sfb + tl.n0, (uint32_t)tl.b_rows * 4u);
+    dma4(rs, (uint32_t)((wave - 4) * 64 + lane) * 4u, st + SB_OFF + (wave - 4) * 256);
+  }
+}
+
+// This lane's LDS offsets within a stage: the two 16-byte chunks of its
+// fragment row (chunks lane/16 and lane/16 + 4 of row lane % 16 of the
+// wave's first band / column block), its row's LHS scale and its four
+// columns' RHS scales.
+struct Offsets {
+  uint32_t a0, a1, b0, b1, sa, sb;
+};
+
+// One K block of a wave's 128 x 64 sub-tile from the stage at `st`.
+__device__ __forceinline__ void block(f32x4 (&acc)[MT][NT], const uint8_t* st, const Offsets& o) {
+  i32x8 bf[NT];
+  f32x4 sb[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const i32x4 x = *reinterpret_cast<const i32x4*>(st + o.b0 + nt * 16 * ROW_BYTES);
+    const i32x4 y = *reinterpret_cast<const i32x4*>(st + o.b1 + nt * 16 * ROW_BYTES);
+    bf[nt] = (i32x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    sb[nt] = *reinterpret_cast<const f32x4*>(st + o.sb + nt * 64);
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const i32x4 x = *reinterpret_cast<const i32x4*>(st + o.a0 + mt * 16 * ROW_BYTES);
+    const i32x4 y = *reinterpret_cast<const i32x4*>(st + o.a1 + mt * 16 * ROW_BYTES);
+    const i32x8 af = (i32x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    const float sa = *reinterpret_cast<const float*>(st + o.sa + mt * 64);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const f32x4 part =
+          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+      acc[mt][nt] += part * (sb[nt] * sa);
+    }
+  }
+}
+
+template <bool HAS_C>
+__global__ void __launch_bounds__(THREADS, 1) k_grouped_kernel(KGroupedArgs p) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave / WAVES_N) * WM;
+  const int wn0 = (wave % WAVES_N) * WN;
+
+  const int row0 = wave * 8 + (lane >> 3);
+  const uint32_t lane_off =
+      (uint32_t)row0 * (uint32_t)p.k + (uint32_t)(((lane & 7) ^ ((row0 >> 1) & 7)) * 16);  // same for every j
+  const int r = lane & 15, q = lane >> 4;
+  Offsets o;
+  o.a0 = (uint32_t)(wm0 * ROW_BYTES + lds_offset(r, q));
+  o.a1 = (uint32_t)(wm0 * ROW_BYTES + lds_offset(r, q + 4));
+  o.b0 = (uint32_t)(A_BYTES + wn0 * ROW_BYTES + lds_offset(r, q));
+  o.b1 = (uint32_t)(A_BYTES + wn0 * ROW_BYTES + lds_offset(r, q + 4));
+  o.sa = (uint32_t)(SA_OFF + 4 * (wm0 + r));
+  o.sb = (uint32_t)(SB_OFF + 4 * (wn0 + 4 * q));
+
+  // XCD-aware rank, as in the other kernels.
+  const int grid = gridDim.x;
+  int rank = blockIdx.x;
+  if ((grid & 7) == 0) rank = (blockIdx.x & 7) * (grid >> 3) + (blockIdx.x >> 3);
+
+  const uint32_t base = lds_addr();
+  const uint8_t* const buf = lds();
+  for (int t = rank; t < p.num_tiles; t += grid) {
+    const Tile tl = tile_at(p, t);
+    const bool on = tl.m0 + wm0 < p.m && tl.n0 + wn0 < p.n;
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    // No wave still reads the previous tile's stages.
+    __syncthreads();
+    if (tl.nkb > 0) issue_block(p, tl, tl.kb0, base, wave, lane, lane_off);
+    for (int i = 0; i < tl.nkb; ++i) {
+      // Block i has landed for every wave (each waits for its own loads,
+      // then all meet), and nobody reads the other stage any more.
+      __syncthreads();
+      if (i + 1 < tl.nkb)
+        issue_block(p, tl, tl.kb0 + i + 1, base + ((i + 1) & 1) * STAGE_BYTES, wave, lane, lane_off);
+      if (on) block(acc, buf + (i & 1) * STAGE_BYTES, o);
+    }
+
+    if (on) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = tl.m0 + wm0 + mt * 16 + r;
+        if (m >= p.m) continue;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const size_t idx = ((size_t)tl.g * p.m + m) * p.n + tl.n0 + wn0 + nt * 16 + 4 * q;
+          f32x4 v = acc[mt][nt];
+          if constexpr (HAS_C) v += *reinterpret_cast<const f32x4*>(p.c + idx);
+          *reinterpret_cast<f32x4*>(p.d + idx) = v;
+        }
+      }
+    }
+  }
+  // Loads issued past the last block read: none (every issued block is read).
+  wait_vmcnt_0();
+}
+
+}  // namespace kgrouped
+
+hipError_t launch_k_grouped(KGroupedArgs& args, int num_cus, hipStream_t stream) {
+  using namespace kgrouped;
+  args.m_blocks = (args.m + BM - 1) / BM;
+  args.n_blocks = (args.n + BN - 1) / BN;
+  args.num_tiles = args.num_groups * args.m_blocks * args.n_blocks;
+  auto kern = args.c ? k_grouped_kernel<true> : k_grouped_kernel<false>;
+  int per_cu = 1;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, THREADS, 0);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) per_cu = 1;
+  const long long slots = (long long)num_cus * per_cu;
+  int grid = (int)(args.num_tiles < slots ? args.num_tiles : slots);
+  if (grid < 1) return hipSuccess;
+  if (grid > 8) grid -= grid & 7;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), 0, stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace dg

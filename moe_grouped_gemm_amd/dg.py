@@ -32,6 +32,7 @@ SIGNATURES = [
     ("dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     ("dg_m_grouped_fp8_gemm_nt_masked_ue8m0", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     ("dg_m_grouped_fp8_gemm_nt_nopad_ue8m0", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
+    ("dg_k_grouped_fp8_gemm_nt_contiguous", [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_i), _i, _i, _i, _vp], _i),
     ("dg_get_mk_alignment_for_contiguous_layout", [], _i),
     ("dg_get_tma_aligned_size", [_i, _i], _i),
     ("dg_get_num_cus", [], _i),
@@ -227,6 +228,39 @@ def m_grouped_fp8_gemm_nt_nopad(a, sfa, b, sfb, d, group_rows, ue8m0: bool = Fal
     return d
 
 
+def k_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, ks, c=None) -> torch.Tensor:
+    """K-grouped GEMM (weight-gradient shape): for each group g,
+    d[g] = (c[g] or 0) + A[:, K_g] . B[:, K_g]^T with per-row, per-128-K
+    scales on both operands. a [M, K], sfa [K/128, tma_aligned(M)],
+    b [N, K], sfb [K/128, tma_aligned(N)], d [G, M, N] float32; ks: the
+    groups' K sizes as host integers (multiples of 128, summing to K);
+    c: None, d itself (accumulate in place) or a separate [G, M, N] float32."""
+    dev = a.device
+    m, k = a.shape
+    n = b.shape[0]
+    ks = [int(x) for x in ks]
+    g = len(ks)
+    _need(a, "a", torch.float8_e4m3fn, 2, dev)
+    _need(b, "b", torch.float8_e4m3fn, 2, dev)
+    _need(sfa, "sfa", torch.float32, 2, dev)
+    _need(sfb, "sfb", torch.float32, 2, dev)
+    _need(d, "d", torch.float32, 3, dev)
+    if c is not None:
+        _need(c, "c", torch.float32, 3, dev)
+        if tuple(c.shape) != tuple(d.shape):
+            raise ValueError("c and d shapes differ")
+    if b.shape[1] != k or tuple(d.shape) != (g, m, n) or sum(ks) != k:
+        raise ValueError("shape mismatch between a, b, d and ks")
+    if (tuple(sfa.shape) != (k // 128, get_tma_aligned_size(m, 4))
+            or tuple(sfb.shape) != (k // 128, get_tma_aligned_size(n, 4))):
+        raise ValueError("scale shapes do not match the (1, 1, 128) recipe layout")
+    ks_arr = (ctypes.c_int * max(g, 1))(*ks)
+    _check(lib().dg_k_grouped_fp8_gemm_nt_contiguous(
+        a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(), None if c is None else c.data_ptr(),
+        d.data_ptr(), ks_arr, g, m, n, _stream(a)), "dg_k_grouped_fp8_gemm_nt_contiguous")
+    return d
+
+
 def run_workload(w, d: torch.Tensor) -> torch.Tensor:
     """Runs the GEMM that matches a synth workload (Dense / Contiguous /
     Masked / Nopad)."""
@@ -240,4 +274,7 @@ def run_workload(w, d: torch.Tensor) -> torch.Tensor:
         return m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m, ue8m0=e8)
     if kind == "Nopad":
         return m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows, ue8m0=e8)
+    if kind == "KGrouped":
+        # the weight-gradient use: accumulate into d in place
+        return k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.ks, c=d)
     raise TypeError(kind)

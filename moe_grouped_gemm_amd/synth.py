@@ -227,6 +227,33 @@ class Nopad:
                 + self.valid_rows() * (k + 4 * (k // BLOCK) + 2 * n) + 4 * self.num_groups)
 
 
+@dataclass
+class KGrouped:
+    a: torch.Tensor          # [M, K]: each group's K columns back to back
+    sfa: torch.Tensor        # [K/128, tma_aligned(M)]
+    b: torch.Tensor          # [N, K]
+    sfb: torch.Tensor        # [K/128, tma_aligned(N)]
+    ks: List[int]            # K of each group (multiples of 128)
+    m: int
+    n: int
+    k: int
+    num_groups: int
+    seed: int = 0
+
+    def new_output(self) -> torch.Tensor:
+        """A float32 [G, M, N] accumulator with seeded N(0, 1) starting values."""
+        return _randn((self.num_groups, self.m, self.n), self.seed, 7, self.a.device)
+
+    def flops(self) -> float:
+        return 2.0 * self.m * self.n * self.k
+
+    def algorithmic_bytes(self) -> float:
+        """Operands and scales once, D written and its prior value read
+        (the in-place accumulation of the benchmark)."""
+        m, n, k = self.m, self.n, self.k
+        return (m + n) * (k + 4 * (k // BLOCK)) + 2 * 4 * self.num_groups * m * n
+
+
 def sentinel_output(shape, device) -> torch.Tensor:
     """A BF16 output buffer prefilled with the 0xFFFF sentinel."""
     return torch.full(shape, -1, dtype=torch.int16, device=device).view(torch.bfloat16)
@@ -304,6 +331,19 @@ def make_nopad(rows: List[int], n: int, k: int, seed: int = 0, device="cpu", tai
     return w
 
 
+def make_k_grouped(ks: List[int], m: int, n: int, seed: int = 0, device="cpu") -> KGrouped:
+    """K-grouped operands: A [M, K] and B [N, K] with one scale per row and
+    128-wide K block for both (recipe (1, 1, 128)): each is quantised like
+    the LHS of the other GEMMs."""
+    k = int(sum(ks))
+    assert all(x % BLOCK == 0 and x >= 0 for x in ks)
+    a, sfa = quantize_lhs(_randn((m, max(k, BLOCK)), seed, 11, device))
+    b, sfb = quantize_lhs(_randn((n, max(k, BLOCK)), seed, 12, device))
+    a, b = a[:, :k].contiguous(), b[:, :k].contiguous()
+    sfa, sfb = sfa[:k // BLOCK].contiguous(), sfb[:k // BLOCK].contiguous()
+    return KGrouped(a, sfa, b, sfb, list(map(int, ks)), m, n, k, len(ks), seed)
+
+
 # ---------------------------------------------------------------------------
 # The benchmark workloads
 # ---------------------------------------------------------------------------
@@ -343,7 +383,10 @@ def workload_spec(index: int, seed: int = 0) -> WorkloadSpec:
     4 contiguous, 32 groups with Zipf(1.2) rows totalling 65536, N=4096, K=7168;
     5 no-padding layout of workload 2's groups (the same row counts, not padded);
     6, 7, 8: workloads 1, 2 and 3 with power-of-two (UE8M0-cast) scales, for
-    the *_ue8m0 entry points.
+    the *_ue8m0 entry points;
+    9 K-grouped weight gradient of workload 2's up projection: 8 groups with
+      K = workload 2's row counts rounded up to 128, M = 4096 (output
+      features), N = 7168 (input features), accumulated into D in place.
     """
     if index == 0:
         return WorkloadSpec(0, "dense", "dense_128x256x512", n=256, k=512, m=128)
@@ -365,10 +408,15 @@ def workload_spec(index: int, seed: int = 0) -> WorkloadSpec:
         base = workload_spec(index - 5, seed)
         return WorkloadSpec(index, base.kind, base.name + "_ue8m0", n=base.n, k=base.k, m=base.m, rows=base.rows,
                             counts=base.counts, max_m=base.max_m, extra={"ue8m0": True})
+    if index == 9:
+        rows = workload_spec(2, seed).rows
+        ks = [(r + BLOCK - 1) // BLOCK * BLOCK for r in rows]
+        return WorkloadSpec(9, "k_grouped", "k_grouped_8x[3000,5000]_m4096_n7168", n=7168, k=int(sum(ks)), m=4096,
+                            rows=ks)
     raise ValueError(f"no workload {index}")
 
 
-NUM_WORKLOADS = 9
+NUM_WORKLOADS = 10
 
 
 def make_workload(spec: WorkloadSpec, seed: int = 0, device="cpu"):
@@ -381,6 +429,8 @@ def make_workload(spec: WorkloadSpec, seed: int = 0, device="cpu"):
         return make_masked(spec.counts, spec.max_m, spec.n, spec.k, seed, device, ue8m0=e8)
     if spec.kind == "nopad":
         return make_nopad(spec.rows, spec.n, spec.k, seed, device, ue8m0=e8)
+    if spec.kind == "k_grouped":
+        return make_k_grouped(spec.rows, spec.m, spec.n, seed, device)
     raise ValueError(spec.kind)
 
 

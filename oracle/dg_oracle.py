@@ -30,7 +30,9 @@ Sources on the pages:
   * "DeepGEMM Compatibility Wrapper (deep-gemm)" page, "0.2.7 Compatibility
     Additions" and "Contiguous Grouped GEMM Alignment": scale recipe
     (1, 128, 128) and the 128-row segment alignment; UE8M0 scale casting and
-    the packed UE8M0 scale conversion (the *_ue8m0 variants below).
+    the packed UE8M0 scale conversion (the *_ue8m0 variants below); the
+    contiguous K-grouped FP8 NT GEMM with host K sizes, recipe (1, 1, 128)
+    and a float32 C (k_grouped_fp8_gemm_nt_contiguous below).
 
 The 128-K block structure of the scales does not change the definition: the
 per-block sums scaled and added are algebraically the plain sum over the
@@ -55,6 +57,12 @@ design notes of the repository):
     biased exponent field, as the packed UE8M0 conversion reads it (sign and
     mantissa bits dropped; e = 255 is NaN). The GEMM is then the same
     definition with those scale values.
+  * K-grouped GEMM: the groups split K into consecutive ranges in the order
+    given; group g's output is D[g] = C[g] + (A restricted to its K range)
+    times (B restricted to it) transposed, with one float32 scale per row
+    and 128-wide K block for both operands (stored transposed like the LHS
+    scales); C absent means zero; the result is float32 and is compared
+    unrounded.
 """
 
 from __future__ import annotations
@@ -85,6 +93,9 @@ __all__ = [
     "m_grouped_fp8_gemm_nt_contiguous_ue8m0",
     "m_grouped_fp8_gemm_nt_masked_ue8m0",
     "m_grouped_fp8_gemm_nt_nopad_ue8m0",
+    "k_grouped_ranges",
+    "k_grouped_fp8_gemm_nt_contiguous",
+    "k_grouped_f64_at",
 ]
 
 # Scale granularity along K for both operands: recipe (1, 128, 128).
@@ -385,3 +396,61 @@ def m_grouped_fp8_gemm_nt_masked_ue8m0(a_codes, sfa, b_codes, sfb, masked_m, d_i
 
 def m_grouped_fp8_gemm_nt_nopad_ue8m0(a_codes, sfa, b_codes, sfb, group_rows, d_init) -> np.ndarray:
     return m_grouped_fp8_gemm_nt_nopad(a_codes, e8m0_value(sfa), b_codes, e8m0_value(sfb), group_rows, d_init)
+
+
+# ---------------------------------------------------------------------------
+# K-grouped GEMM (weight-gradient shape), recipe (1, 1, 128)
+# ---------------------------------------------------------------------------
+
+def k_grouped_ranges(ks) -> list:
+    """[first, end) of each group's K positions: consecutive, in order."""
+    out, start = [], 0
+    for x in ks:
+        out.append((start, start + int(x)))
+        start += int(x)
+    return out
+
+
+def _k_group_operands(a_codes, sfa, b_codes, sfb, k0, k1):
+    """Dequantised A[:, k0:k1] and B[:, k0:k1]: one scale per row and
+    128-wide K block for both, sf[k // 128][row]."""
+    kb0, kb1 = k0 // BLOCK_K, k1 // BLOCK_K
+    ahat = dequant_lhs(a_codes[:, k0:k1], sfa[kb0:kb1])
+    bhat = dequant_lhs(b_codes[:, k0:k1], sfb[kb0:kb1])
+    return ahat, bhat
+
+
+def k_grouped_fp8_gemm_nt_contiguous(a_codes, sfa, b_codes, sfb, ks, c_init=None) -> np.ndarray:
+    """K-grouped FP8 NT GEMM, float64 result [G, M, N].
+
+    a_codes [M, K], sfa [K/128, ld >= M], b_codes [N, K], sfb [K/128, ld >= N],
+    ks: the groups' K sizes (multiples of 128, summing to K), c_init None or
+    [G, M, N]. D[g] = c_init[g] (or 0) + sum_{k in group g} Ahat[:, k] Bhat[:, k]^T.
+    """
+    m_rows, k = a_codes.shape
+    n = b_codes.shape[0]
+    ranges = k_grouped_ranges(ks)
+    assert ranges[-1][1] == k and all((e - f) % BLOCK_K == 0 for f, e in ranges)
+    d = np.zeros((len(ranges), m_rows, n)) if c_init is None else np.array(c_init, dtype=np.float64, copy=True)
+    for g, (k0, k1) in enumerate(ranges):
+        if k1 > k0:
+            ahat, bhat = _k_group_operands(a_codes, sfa, b_codes, sfb, k0, k1)
+            d[g] += ahat @ bhat.T
+    return d
+
+
+def k_grouped_f64_at(a_codes, sfa, b_codes, sfb, ks, group, rows, cols, c_init=None, abs_sum=False):
+    """Group `group`'s result at rows x cols (float64); with abs_sum also
+    sum_k |Ahat[r, k] Bhat[c, k]| + |C| there (for error bounds)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    k0, k1 = k_grouped_ranges(ks)[group]
+    c = np.zeros((rows.size, cols.size)) if c_init is None else np.asarray(c_init, np.float64)[group][np.ix_(rows, cols)]
+    if k1 == k0:
+        val, mag = c.copy(), np.abs(c)
+    else:
+        ahat = dequant_lhs(a_codes[rows][:, k0:k1], sfa[k0 // BLOCK_K:k1 // BLOCK_K][:, rows])
+        bhat = dequant_lhs(b_codes[cols][:, k0:k1], sfb[k0 // BLOCK_K:k1 // BLOCK_K][:, cols])
+        val = c + ahat @ bhat.T
+        mag = np.abs(c) + np.abs(ahat) @ np.abs(bhat).T
+    return (val, mag) if abs_sum else val

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = dg.lib()
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(n for n, _, _ in dg.SIGNATURES) == names
@@ -140,6 +140,29 @@ def test_ue8m0_variants_share_the_checks():
         assert call(a=None) == 1, name
         assert call(a=A + 8) == 3, name
         assert call(n=192) == 2, name
+
+
+def test_k_grouped_checks():
+    import ctypes
+    lib = dg.lib()
+
+    def call(a=A, c=None, d=D, ks=(128, 256), g=None, m=256, n=256):
+        arr = (ctypes.c_int * max(len(ks), 1))(*ks)
+        return lib.dg_k_grouped_fp8_gemm_nt_contiguous(a, SFA, B, SFB, c, d, arr, len(ks) if g is None else g,
+                                                       m, n, None)
+    assert call(a=None) == 1
+    assert call(d=None) == 1
+    assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(A, SFA, B, SFB, None, D, None, 2, 256, 256, None) == 1
+    assert call(ks=(), g=0) == 2         # an empty K-size list is rejected
+    assert call(ks=(100, 128)) == 2      # K sizes are multiples of 128
+    assert call(ks=(-128, 256)) == 2
+    assert call(n=192) == 2
+    assert call(m=-1) == 2
+    assert call(ks=(1 << 20, 128)) == 4  # total K beyond the limit
+    assert call(ks=(128,) * 513) == 4    # more than 512 groups
+    assert call(c=D + 4) == 3
+    assert call(a=A + 8) == 3
+    assert call(m=0) == 0                # empty: a successful no-op
 
 
 def test_no_device_reported_without_gpu():

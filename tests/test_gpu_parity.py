@@ -455,6 +455,79 @@ def test_ue8m0_close_to_float32_path(dev):
 
 
 # ---------------------------------------------------------------------------
+# K-grouped GEMM (float32 output)
+# ---------------------------------------------------------------------------
+#
+# Tolerance. The MFMA does not sum a K block's 128 FP8 products as rounded
+# float32 additions: measured on MI355X, one block's result is off by up to
+# 1.6e-5 (about 2^-16) of the sum of the products' magnitudes (that limited
+# accumulation precision is why the method promotes every 128-K block into
+# float32 registers). Allowing 2^-15 of that per block, plus the float32
+# promotion (sfb * sfa, the product and the add: 3 roundings per block) and
+# the rounding of C, every element satisfies
+#   |D - R| <= (2^-15 + (nkb + 3) * 2^-24) * sum_k |Ahat Bhat| + 2^-24 * |C|
+# with R the float64 oracle and nkb the group's K blocks. The relative
+# Frobenius error must stay below 5e-5 (measured: 1.35e-5).
+
+def _check_k_grouped(w, d, c0, what, groups=None, rows=None, cols=None):
+    got = d.detach().cpu().numpy().astype(np.float64)
+    c_np = None if c0 is None else c0.detach().cpu().numpy()
+    rows = np.arange(w.m) if rows is None else rows
+    cols = np.arange(w.n) if cols is None else cols
+    a, sfa, b, sfb = NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb)
+    for g in (range(w.num_groups) if groups is None else groups):
+        ref, mag = O.k_grouped_f64_at(a, sfa, b, sfb, w.ks, g, rows, cols, c_np, abs_sum=True)
+        cmag = 0.0 if c_np is None else np.abs(c_np[g][np.ix_(rows, cols)])
+        out = got[g][np.ix_(rows, cols)]
+        nkb = w.ks[g] // 128
+        bound = (2.0 ** -15 + (nkb + 3) * 2.0 ** -24) * (mag - cmag) + 2.0 ** -24 * cmag + 1e-30
+        bad = np.abs(out - ref) > bound
+        assert not bad.any(), f"{what} group {g}: {int(bad.sum())} elements beyond the bound"
+        nr = np.linalg.norm(ref)
+        if nr > 0:
+            assert np.linalg.norm(out - ref) <= 5e-5 * nr, f"{what} group {g}: relative Frobenius error"
+
+
+@pytest.mark.parametrize("ks,m,n", [
+    ([128, 0, 384, 256], 300, 384),
+    ([4096], 130, 256),
+    ([256, 128], 1, 128),
+    ([512, 1024, 128], 520, 640),
+])
+@pytest.mark.parametrize("c_mode", ["none", "separate", "in_place"])
+def test_k_grouped_small(dev, ks, m, n, c_mode):
+    _say(f"k_grouped ks={ks} m={m} n={n} c={c_mode}")
+    w = synth.make_k_grouped(ks, m, n, seed=m + len(ks), device=dev)
+    d = w.new_output()
+    c0 = None if c_mode == "none" else d.clone()
+    if c_mode == "none":
+        d.fill_(float("nan"))             # every element must be written
+        dg.k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.ks)
+    elif c_mode == "separate":
+        out = torch.full_like(d, float("nan"))
+        dg.k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, out, w.ks, c=d)
+        torch.cuda.synchronize()
+        assert torch.equal(d, c0), "C was modified"
+        d = out
+    else:
+        dg.k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.ks, c=d)
+    torch.cuda.synchronize()
+    _check_k_grouped(w, d, c0, f"k_grouped {ks} {c_mode}")
+
+
+def test_k_grouped_many_groups(dev):
+    rng = np.random.default_rng(59)
+    ks = [int(x) * 128 for x in rng.integers(0, 3, size=40)]
+    _say(f"k_grouped {len(ks)} groups, K={sum(ks)}")
+    w = synth.make_k_grouped(ks, 64, 128, seed=5, device=dev)
+    d = w.new_output()
+    c0 = d.clone()
+    dg.k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.ks, c=d)
+    torch.cuda.synchronize()
+    _check_k_grouped(w, d, c0, "k_grouped many groups")
+
+
+# ---------------------------------------------------------------------------
 # The benchmark workloads at full size (sampled comparison)
 # ---------------------------------------------------------------------------
 
@@ -470,9 +543,15 @@ def test_workload_full_size(dev, index):
     _say(f"workload {index} {spec.name}")
     w = synth.make_workload(spec, seed=0, device=dev)
     d = w.new_output()
+    c0 = d.clone() if spec.kind == "k_grouped" else None
     dg.run_workload(w, d)
     torch.cuda.synchronize()
     rng = np.random.default_rng(100 + index)
+    if spec.kind == "k_grouped":
+        rows = _sample(w.m, 24, rng, (0, 255, 256, w.m - 1))
+        cols = _sample(w.n, 24, rng, (0, 255, 256, w.n - 1))
+        _check_k_grouped(w, d, c0, spec.name, rows=rows, cols=cols)
+        return
     got = NP(d)
     a, sfa, b, sfb = NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb)
     if w.ue8m0:

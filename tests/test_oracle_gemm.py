@@ -14,7 +14,10 @@ Each pin checks the oracle against something other than its own code:
   * a no-padding row owner map built by walking the counts row by row;
   * UE8M0 scales: a hand-derived table of float32 bit patterns and their
     E8M0 values (tests/golden/e8m0_scale_cases.txt), the float32 variants on
-    power-of-two scales, and math.frexp rounding down for other scales.
+    power-of-two scales, and math.frexp rounding down for other scales;
+  * K-grouped GEMM: exact rationals with the indices written out, K-range
+    splitting additivity, empty groups, and the dense GEMM as the special
+    case of one group with block-constant RHS scales.
 
 test_planted_mistakes_are_caught plants plausible mistakes in a private copy
 of the oracle (wrong scale index, transposed RHS scales, wrong FP8 flavour,
@@ -383,6 +386,58 @@ def pin_e8m0_golden(orc):
     F.check_e8m0_golden(orc)
 
 
+def pin_exact_k_grouped(orc):
+    """Tiny K-grouped case against exact rationals, indices written out:
+    D[g][i][j] = C[g][i][j] + sum over group g's k of
+    dec(a[i,k]) sfa[k//128, i] dec(b[j,k]) sfb[k//128, j]."""
+    rng = np.random.default_rng(47)
+    ks = [128, 0, 256]
+    m_rows, n, k = 3, 5, sum(ks)
+    a = rng.integers(0, 256, size=(m_rows, k)).astype(np.uint8)
+    b = rng.integers(0, 256, size=(n, k)).astype(np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x30
+    b[(b & 0x7F) == 0x7F] = 0x30
+    sfa = rng.uniform(0.25, 4.0, size=(k // 128, 4)).astype(np.float32)
+    sfb = rng.uniform(0.25, 4.0, size=(k // 128, 8)).astype(np.float32)
+    c = rng.standard_normal((3, m_rows, n)).astype(np.float32)
+    av, bv = _decode_torch(a), _decode_torch(b)
+    d = orc.k_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, ks, c)
+    starts = [0, 128, 128]
+    for g in range(3):
+        for i in range(m_rows):
+            for j in range(n):
+                terms = [Fraction(float(av[i, kk])) * Fraction(float(sfa[kk // 128, i]))
+                         * Fraction(float(bv[j, kk])) * Fraction(float(sfb[kk // 128, j]))
+                         for kk in range(starts[g], starts[g] + ks[g])]
+                exact = Fraction(float(c[g, i, j])) + sum(terms, Fraction(0))
+                bound = (float(sum(abs(t) for t in terms)) + abs(float(c[g, i, j]))) * (k + 2) * 2.0 ** -52
+                assert abs(d[g, i, j] - float(exact)) <= bound, (g, i, j)
+
+
+def pin_k_grouped_invariants(orc):
+    """(1) splitting a group's K range in two and adding the two outputs
+    gives the merged group's; (2) an empty group returns C (zeros without
+    C); (3) one group with RHS scales constant over 128-row blocks of N is
+    the dense GEMM with those block scales."""
+    rng = np.random.default_rng(53)
+    m_rows, n = 6, 256
+    a, _, b, _ = _random_inputs(rng, m_rows, n, 512)
+    sfa = rng.uniform(0.5, 2, size=(4, 8)).astype(np.float32)
+    sfb = rng.uniform(0.5, 2, size=(4, 256)).astype(np.float32)
+    merged = orc.k_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, [128, 384])
+    split = orc.k_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, [128, 128, 256])
+    np.testing.assert_allclose(split[1] + split[2], merged[1], rtol=1e-12, atol=1e-9)
+    np.testing.assert_array_equal(split[0], merged[0])
+    c = rng.standard_normal((3, m_rows, n))
+    with_empty = orc.k_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, [128, 0, 384], c)
+    assert np.array_equal(with_empty[1], c[1])
+    assert np.all(orc.k_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, [0, 512])[0] == 0)
+    blocks = rng.uniform(0.5, 2, size=(n // 128, 4)).astype(np.float32)     # [N/128][K/128]
+    sfb_rows = np.repeat(blocks.T, 128, axis=1)                            # [K/128][N]
+    one = orc.k_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb_rows, [512])[0]
+    np.testing.assert_allclose(one, orc.gemm_nt_f64(a, sfa, b, blocks), rtol=1e-12, atol=1e-9)
+
+
 def pin_contiguous_poisoned_padding(orc):
     rng = np.random.default_rng(17)
     rows = [5, 128, 1]
@@ -449,6 +504,8 @@ PINS = [
     pin_e8m0_golden,
     pin_ue8m0_power_of_two_identity,
     pin_ue8m0_drops_mantissa,
+    pin_exact_k_grouped,
+    pin_k_grouped_invariants,
 ]
 
 
@@ -617,6 +674,31 @@ def _mut_e8m0_keeps_mantissa(mod):
     mod.e8m0_value = f
 
 
+def _mut_k_grouped_restart(mod):
+    # every group reads K from position 0
+    def f(ks):
+        return [(0, int(x)) for x in ks]
+    mod.k_grouped_ranges = f
+
+
+def _mut_k_grouped_rhs_block_scales(mod):
+    # RHS scale of the 128-row block's first row instead of the row's own
+    orig = mod._k_group_operands
+
+    def f(a_codes, sfa, b_codes, sfb, k0, k1):
+        sfb2 = np.repeat(np.asarray(sfb)[:, ::128], 128, axis=1)[:, :np.asarray(sfb).shape[1]]
+        return orig(a_codes, sfa, b_codes, sfb2, k0, k1)
+    mod._k_group_operands = f
+
+
+def _mut_k_grouped_drops_c(mod):
+    orig = mod.k_grouped_fp8_gemm_nt_contiguous
+
+    def f(a_codes, sfa, b_codes, sfb, ks, c_init=None):
+        return orig(a_codes, sfa, b_codes, sfb, ks, None)
+    mod.k_grouped_fp8_gemm_nt_contiguous = f
+
+
 MUTANTS = [
     _mut_lhs_scale_first_row,
     _mut_rhs_scale_transposed,
@@ -634,6 +716,9 @@ MUTANTS = [
     _mut_e8m0_rounds_up,
     _mut_e8m0_bias_128,
     _mut_e8m0_keeps_mantissa,
+    _mut_k_grouped_restart,
+    _mut_k_grouped_rhs_block_scales,
+    _mut_k_grouped_drops_c,
 ]
 
 
