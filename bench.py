@@ -2,13 +2,14 @@
 
 One step = one call of the GEMM on one batch of synthetic input already in
 HBM. The headline workload is the dense 4096x7168x2048 GEMM; the grouped
-contiguous, masked-decode, no-padding and small dense workloads are measured
-after it and reported under "workloads". Prints ONE JSON line.
+contiguous, masked-decode, no-padding, UE8M0-scale, K-grouped and small dense
+workloads are measured after it and reported under "workloads". Prints ONE
+JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only INDEX]
                     [--no-cpu-baseline] [--no-extra] [--copy-calibration]
 
---only INDEX times a single workload (0..5), for profiling runs.
+--only INDEX times a single workload (0..9), for profiling runs.
 --copy-calibration runs a plain 1 GiB device copy (for scaling HBM traffic
 counters) and exits.
 """
@@ -31,7 +32,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 HEADLINE = 1                 # dense 4096x7168x2048
 # The device code of the kernels (the traffic figures are valid for it only).
 KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_gemm_amd", "csrc", f)
-                  for f in ("dg_device.h", "dg_kernel.hip", "dg_kernel_deep.hip")]
+                  for f in ("dg_device.h", "dg_kernel.hip", "dg_kernel_deep.hip", "dg_kernel_kgrouped.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -186,11 +187,12 @@ def main():
         "dtype": "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": spec.name, "kind": spec.kind, "n": spec.n, "k": spec.k,
-                   **({"m": spec.m} if spec.kind == "dense" else {}),
+                   **({"m": spec.m} if spec.kind in ("dense", "k_grouped") else {}),
                    "accumulate": "fp32 with per-128-K promotion", "output": "bf16", "seed": 0},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "fp8_gemm_nt_kernel", "kernel_ms": round(kernel_ms, 5),
+                     "kernel": "k_grouped_kernel" if spec.kind == "k_grouped" else "fp8_gemm_nt_kernel",
+                     "kernel_ms": round(kernel_ms, 5),
                      "algorithmic_bytes": w.algorithmic_bytes()},
     }
     if spec.kind == "masked":
@@ -204,14 +206,15 @@ def main():
             s = synth.workload_spec(idx)
             wx = synth.make_workload(s, seed=0, device=dev)
             torch.cuda.synchronize()
+            # enough untimed launches for the clocks to settle on each workload
             steps = max(5, args.steps // 4)
-            ms, kms = time_workload(wx, steps, max(2, args.warmup // 10))
+            ms, kms = time_workload(wx, steps, max(2, args.warmup // 3))
             tf = wx.flops() / (kms * 1e-3) / 1e12
             gbs = wx.algorithmic_bytes() / (kms * 1e-3) / 1e9
             extra[s.name] = {"kernel_ms": round(kms, 5), "tflops": round(tf, 2),
                              "fp8_peak_frac": round(tf / FP8_PEAK_TFLOPS, 4),
                              "algorithmic_gbs": round(gbs, 1), "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
-                             "valid_rows": getattr(wx, "valid_rows", lambda: spec.m)() if s.kind != "dense" else s.m}
+                             "valid_rows": getattr(wx, "valid_rows", lambda: s.m)()}
             del wx
             torch.cuda.empty_cache()
         out["workloads"] = extra
