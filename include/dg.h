@@ -175,6 +175,34 @@ dg_status dg_m_grouped_fp8_gemm_nt_nopad_ue8m0(const void* a, const float* sfa,
                                                void* stream);
 
 /*
+ * M-grouped FP8 x FP4 (W4A8) NT GEMMs ("DeepGEMM Compatibility Wrapper"
+ * page, "0.2.7 Compatibility Additions": FP8 E4M3 A with packed E2M1 FP4 B,
+ * LHS scales per 1x128 and RHS scales per 1x32), contiguous and masked
+ * layouts. Everything is as for the FP8 calls of the same layout except B
+ * and its scales:
+ *   b   [num_groups][n][k/2] bytes: OCP E2M1 FP4 values packed two per byte
+ *       along K, element 2j in the low nibble of byte j and 2j+1 in the high
+ *       one (E2M1: sign bit 3, exponent bits 2..1 with bias 1, mantissa bit 0;
+ *       values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives)
+ *   sfb [num_groups][k/32][dg_get_tma_aligned_size(n,4)] float32: one scale
+ *       per row n and 32-wide K block, stored transposed like the LHS scales.
+ * All scales (sfa and sfb) are read as UE8M0, exactly as by the *_ue8m0
+ * calls: 2^(e - 127) with e the float32 exponent field, meant for positive
+ * normal powers of two. Products accumulate in float32 inside the MFMA.
+ *   D = bf16( sum_k e4m3(A[m][k]) sfa[k/128][m] * e2m1(B[n][k]) sfb[k/32][n] )
+ */
+dg_status dg_m_grouped_fp8_fp4_gemm_nt_contiguous(const void* a, const float* sfa,
+                                                  const void* b, const float* sfb,
+                                                  void* d, const int32_t* grouped_layout,
+                                                  int m, int n, int k, int num_groups,
+                                                  void* stream);
+dg_status dg_m_grouped_fp8_fp4_gemm_nt_masked(const void* a, const float* sfa,
+                                              const void* b, const float* sfb,
+                                              void* d, const int32_t* masked_m,
+                                              int num_groups, int max_m, int n, int k,
+                                              void* stream);
+
+/*
  * K-grouped FP8 NT GEMM, contiguous K groups: the weight-gradient shape of
  * an MoE layer ("DeepGEMM Compatibility Wrapper" page, "0.2.7 Compatibility
  * Additions": K sizes given on the host, each a multiple of 128, scale recipe

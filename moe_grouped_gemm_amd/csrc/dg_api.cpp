@@ -202,6 +202,69 @@ dg_status dg_m_grouped_fp8_gemm_nt_nopad_ue8m0(const void* a, const float* sfa, 
   return nopad(a, sfa, b, sfb, d, group_rows, m, n, k, num_groups, true, stream);
 }
 
+dg_status dg_m_grouped_fp8_fp4_gemm_nt_contiguous(const void* a, const float* sfa, const void* b, const float* sfb,
+                                                  void* d, const int32_t* grouped_layout, int m, int n, int k,
+                                                  int num_groups, void* stream) {
+  if (dg_status s = common_checks(a, sfa, b, sfb, d, n, k)) return s;
+  if (!grouped_layout) return DG_ERR_NULL;
+  if (m < 0 || num_groups < 0 || m % 128 != 0) return DG_ERR_SHAPE;
+  if ((long long)m * k >= kMaxBytes || (long long)m * n * 2 >= kMaxBytes ||
+      (long long)num_groups * n * (k / 2) >= kMaxBytes)
+    return DG_ERR_UNSUPPORTED;
+  if (m == 0 || num_groups == 0) return DG_OK;
+  dg::GemmArgs args{};
+  args.a = static_cast<const uint8_t*>(a);
+  args.sfa = sfa;
+  args.b = static_cast<const uint8_t*>(b);
+  args.sfb = sfb;
+  args.d = static_cast<uint16_t*>(d);
+  args.aux = grouped_layout;
+  args.m = m;
+  args.n = n;
+  args.k = k;
+  args.num_groups = num_groups;
+  args.ld_sfa = tma_aligned(m, 4);
+  args.ld_sfb = tma_aligned(n, 4);
+  args.scale_e8m0 = 1;
+  const int cus = effective_cus();
+  if (cus <= 0) return DG_ERR_DEVICE;
+  return dg::launch_fp8_fp4(dg::KIND_CONTIGUOUS, args, cus, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? DG_OK
+             : DG_ERR_LAUNCH;
+}
+
+dg_status dg_m_grouped_fp8_fp4_gemm_nt_masked(const void* a, const float* sfa, const void* b, const float* sfb,
+                                              void* d, const int32_t* masked_m, int num_groups, int max_m, int n,
+                                              int k, void* stream) {
+  if (dg_status s = common_checks(a, sfa, b, sfb, d, n, k)) return s;
+  if (!masked_m) return DG_ERR_NULL;
+  if (num_groups < 0 || max_m <= 0) return DG_ERR_SHAPE;
+  if (num_groups > kMaxMaskedGroups) return DG_ERR_UNSUPPORTED;
+  if ((long long)num_groups * max_m * k >= kMaxBytes || (long long)num_groups * max_m * n * 2 >= kMaxBytes ||
+      (long long)num_groups * n * (k / 2) >= kMaxBytes)
+    return DG_ERR_UNSUPPORTED;
+  if (num_groups == 0) return DG_OK;
+  dg::GemmArgs args{};
+  args.a = static_cast<const uint8_t*>(a);
+  args.sfa = sfa;
+  args.b = static_cast<const uint8_t*>(b);
+  args.sfb = sfb;
+  args.d = static_cast<uint16_t*>(d);
+  args.aux = masked_m;
+  args.m = max_m;
+  args.n = n;
+  args.k = k;
+  args.num_groups = num_groups;
+  args.ld_sfa = tma_aligned(max_m, 4);
+  args.ld_sfb = tma_aligned(n, 4);
+  args.scale_e8m0 = 1;
+  const int cus = effective_cus();
+  if (cus <= 0) return DG_ERR_DEVICE;
+  return dg::launch_fp8_fp4(dg::KIND_MASKED, args, cus, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? DG_OK
+             : DG_ERR_LAUNCH;
+}
+
 dg_status dg_k_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, const void* b, const float* sfb,
                                               const float* c, float* d, const int* ks, int num_groups, int m, int n,
                                               void* stream) {

@@ -32,10 +32,15 @@ struct GemmArgs {
   int m;               // dense/contiguous/no-padding: rows of A and D; masked: max_m
   int n, k, num_groups;
   int ld_sfa;          // leading dimension of the transposed LHS scales
+  int ld_sfb;          // FP8 x FP4 GEMMs only: leading dimension of the per-32-K RHS scales
   int scale_e8m0;      // nonzero: every scale is used as 2^(its exponent field - 127), applied
                        // by the MFMA itself (E8M0 block scales) instead of a float32 promotion
   int m_blocks, n_blocks, num_tiles;  // filled in by launch_gemm
 };
+
+// Enqueues the FP8 x FP4 (W4A8) grouped GEMM of layout `kind` (contiguous or
+// masked) on `stream` (dg_kernel_fp4.hip); arguments already validated.
+hipError_t launch_fp8_fp4(int kind, GemmArgs args, int num_cus, hipStream_t stream);
 
 // Largest group count of the K-grouped GEMM (its group offsets travel in the
 // kernel arguments).

@@ -32,6 +32,8 @@ SIGNATURES = [
     ("dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     ("dg_m_grouped_fp8_gemm_nt_masked_ue8m0", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     ("dg_m_grouped_fp8_gemm_nt_nopad_ue8m0", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
+    ("dg_m_grouped_fp8_fp4_gemm_nt_contiguous", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
+    ("dg_m_grouped_fp8_fp4_gemm_nt_masked", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     ("dg_k_grouped_fp8_gemm_nt_contiguous", [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_i), _i, _i, _i, _vp], _i),
     ("dg_get_mk_alignment_for_contiguous_layout", [], _i),
     ("dg_get_tma_aligned_size", [_i, _i], _i),
@@ -228,6 +230,54 @@ def m_grouped_fp8_gemm_nt_nopad(a, sfa, b, sfb, d, group_rows, ue8m0: bool = Fal
     return d
 
 
+def m_grouped_fp8_fp4_gemm_nt_contiguous(a, sfa, b, sfb, d, grouped_layout) -> torch.Tensor:
+    """FP8 x FP4 (W4A8) contiguous-layout grouped GEMM: as the FP8 call, with
+    b [G, N, K/2] uint8 (packed E2M1, element 2j in the low nibble of byte j)
+    and sfb [G, K/32, tma_aligned(N)] float32; every scale is read as UE8M0."""
+    dev = a.device
+    m, k = a.shape
+    g, n, kh = b.shape
+    _need(a, "a", torch.float8_e4m3fn, 2, dev)
+    _need(b, "b", torch.uint8, 3, dev)
+    _need(sfa, "sfa", torch.float32, 2, dev)
+    _need(sfb, "sfb", torch.float32, 3, dev)
+    _need(d, "d", torch.bfloat16, 2, dev)
+    _need(grouped_layout, "grouped_layout", torch.int32, 1, dev)
+    if kh * 2 != k or tuple(d.shape) != (m, n) or grouped_layout.shape[0] != m:
+        raise ValueError("shape mismatch between a, b, d and grouped_layout")
+    if (tuple(sfa.shape) != (k // 128, get_tma_aligned_size(m, 4))
+            or tuple(sfb.shape) != (g, k // 32, get_tma_aligned_size(n, 4))):
+        raise ValueError("scale shapes do not match the (1, 128) x (1, 32) layout")
+    _check(lib().dg_m_grouped_fp8_fp4_gemm_nt_contiguous(
+        a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(), d.data_ptr(), grouped_layout.data_ptr(),
+        m, n, k, g, _stream(a)), "dg_m_grouped_fp8_fp4_gemm_nt_contiguous")
+    return d
+
+
+def m_grouped_fp8_fp4_gemm_nt_masked(a, sfa, b, sfb, d, masked_m) -> torch.Tensor:
+    """FP8 x FP4 (W4A8) masked-layout grouped GEMM: a [G, max_m, K],
+    sfa [G, K/128, tma_aligned(max_m)], b [G, N, K/2] uint8 (packed E2M1),
+    sfb [G, K/32, tma_aligned(N)], d [G, max_m, N]; every scale read as UE8M0."""
+    dev = a.device
+    g, max_m, k = a.shape
+    n = b.shape[1]
+    _need(a, "a", torch.float8_e4m3fn, 3, dev)
+    _need(b, "b", torch.uint8, 3, dev)
+    _need(sfa, "sfa", torch.float32, 3, dev)
+    _need(sfb, "sfb", torch.float32, 3, dev)
+    _need(d, "d", torch.bfloat16, 3, dev)
+    _need(masked_m, "masked_m", torch.int32, 1, dev)
+    if b.shape[0] != g or b.shape[2] * 2 != k or tuple(d.shape) != (g, max_m, n) or masked_m.shape[0] != g:
+        raise ValueError("shape mismatch between a, b, d and masked_m")
+    if (tuple(sfa.shape) != (g, k // 128, get_tma_aligned_size(max_m, 4))
+            or tuple(sfb.shape) != (g, k // 32, get_tma_aligned_size(n, 4))):
+        raise ValueError("scale shapes do not match the (1, 128) x (1, 32) layout")
+    _check(lib().dg_m_grouped_fp8_fp4_gemm_nt_masked(
+        a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(), d.data_ptr(), masked_m.data_ptr(),
+        g, max_m, n, k, _stream(a)), "dg_m_grouped_fp8_fp4_gemm_nt_masked")
+    return d
+
+
 def k_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, ks, c=None) -> torch.Tensor:
     """K-grouped GEMM (weight-gradient shape): for each group g,
     d[g] = (c[g] or 0) + A[:, K_g] . B[:, K_g]^T with per-row, per-128-K
@@ -266,6 +316,10 @@ def run_workload(w, d: torch.Tensor) -> torch.Tensor:
     Masked / Nopad)."""
     kind = type(w).__name__
     e8 = getattr(w, "ue8m0", False)
+    if getattr(w, "fp4", False):
+        if kind == "Contiguous":
+            return m_grouped_fp8_fp4_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout)
+        return m_grouped_fp8_fp4_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m)
     if kind == "Dense":
         return fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d, ue8m0=e8)
     if kind == "Contiguous":

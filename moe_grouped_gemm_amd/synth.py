@@ -80,6 +80,34 @@ def quantize_rhs(x: torch.Tensor, ue8m0: bool = False):
     return q.view(n, k), scale.contiguous()
 
 
+FP4_MAX = 6.0        # largest OCP E2M1 value
+FP4_BLOCK = 32       # RHS scale granularity along K of the FP8 x FP4 GEMMs
+
+
+def quantize_rhs_e2m1(x: torch.Tensor):
+    """x float32 [N, K] -> (b uint8 [N, K/2]: OCP E2M1 codes packed two per
+    byte, element 2j in the low nibble of byte j; sfb float32 [K/32,
+    tma_aligned(N)]: one power-of-two scale per row and 32-wide K block,
+    rounded up from amax / 6). Values round to the nearest E2M1 value, ties
+    to the even code."""
+    n, k = x.shape
+    assert k % BLOCK == 0
+    xb = x.view(n, k // FP4_BLOCK, FP4_BLOCK)
+    scale = pow2_ceil(xb.abs().amax(dim=-1).clamp(min=SCALE_FLOOR) / FP4_MAX)   # [N, K/32]
+    y = (xb / scale.unsqueeze(-1)).clamp(-FP4_MAX, FP4_MAX)
+    a = y.abs()
+    # E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 (codes 0..7); at each midpoint
+    # the even code wins: ">" where the lower code is even, ">=" where the upper is
+    code = ((a > 0.25).int() + (a >= 0.75).int() + (a > 1.25).int() + (a >= 1.75).int()
+            + (a > 2.5).int() + (a >= 3.5).int() + (a > 5.0).int())
+    code = code | ((y < 0) & (code > 0)).int() * 8
+    code = code.view(n, k).to(torch.uint8)
+    packed = code[:, 0::2] | (code[:, 1::2] << 4)
+    sfb = torch.zeros(k // FP4_BLOCK, tma_aligned_size(n), dtype=torch.float32, device=x.device)
+    sfb[:, :n] = scale.t()
+    return packed.contiguous(), sfb
+
+
 def _gen(seed: int, stream: int, device) -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(int(seed) * 1000003 + int(stream))
@@ -90,7 +118,20 @@ def _randn(shape, seed, stream, device) -> torch.Tensor:
     return torch.randn(*shape, generator=_gen(seed, stream, device), dtype=torch.float32, device=device)
 
 
-def _quantize_rhs_grouped(num_groups: int, n: int, k: int, seed: int, device, ue8m0: bool = False):
+def _quantize_rhs_grouped_fp4(num_groups: int, n: int, k: int, seed: int, device):
+    b = torch.empty(num_groups, n, k // 2, dtype=torch.uint8, device=device)
+    sfb = torch.zeros(num_groups, k // FP4_BLOCK, tma_aligned_size(n), dtype=torch.float32, device=device)
+    for g in range(num_groups):
+        bq, s = quantize_rhs_e2m1(_randn((n, k), seed, 100 + g, device))
+        b[g].copy_(bq)
+        sfb[g].copy_(s)
+    return b, sfb
+
+
+def _quantize_rhs_grouped(num_groups: int, n: int, k: int, seed: int, device, ue8m0: bool = False,
+                          fp4: bool = False):
+    if fp4:
+        return _quantize_rhs_grouped_fp4(num_groups, n, k, seed, device)
     b = torch.empty(num_groups, n, k, dtype=torch.float8_e4m3fn, device=device)
     sfb = torch.empty(num_groups, n // BLOCK, k // BLOCK, dtype=torch.float32, device=device)
     for g in range(num_groups):
@@ -103,6 +144,13 @@ def _quantize_rhs_grouped(num_groups: int, n: int, k: int, seed: int, device, ue
 # ---------------------------------------------------------------------------
 # Workload containers
 # ---------------------------------------------------------------------------
+
+def _b_bytes(n: int, k: int, fp4: bool) -> int:
+    """Bytes of one group's B and its scales."""
+    if fp4:
+        return n * k // 2 + 4 * n * (k // FP4_BLOCK)
+    return n * k + 4 * (n // BLOCK) * (k // BLOCK)
+
 
 @dataclass
 class Dense:
@@ -139,6 +187,7 @@ class Contiguous:
     k: int
     num_groups: int
     ue8m0: bool = False
+    fp4: bool = False        # B packed E2M1 [G, N, K/2] with sfb [G, K/32, tma_aligned(N)]
 
     def new_output(self) -> torch.Tensor:
         return sentinel_output((self.m, self.n), self.a.device)
@@ -152,7 +201,7 @@ class Contiguous:
     def algorithmic_bytes(self) -> float:
         n, k = self.n, self.k
         used = sum(1 for r in self.rows if r > 0)
-        return (used * (n * k + 4 * (n // BLOCK) * (k // BLOCK))
+        return (used * _b_bytes(n, k, self.fp4)
                 + self.valid_rows() * (k + 4 * (k // BLOCK) + 2 * n) + 4 * self.m)
 
 
@@ -169,6 +218,7 @@ class Masked:
     k: int
     num_groups: int
     ue8m0: bool = False
+    fp4: bool = False
 
     def new_output(self) -> torch.Tensor:
         return sentinel_output((self.num_groups, self.max_m, self.n), self.a.device)
@@ -182,7 +232,7 @@ class Masked:
     def algorithmic_bytes(self) -> float:
         n, k = self.n, self.k
         used = sum(1 for c in self.counts if c > 0)
-        return (used * (n * k + 4 * (n // BLOCK) * (k // BLOCK))
+        return (used * _b_bytes(n, k, self.fp4)
                 + self.valid_rows() * (k + 4 * (k // BLOCK) + 2 * n) + 4 * self.num_groups)
 
 
@@ -282,7 +332,10 @@ def contiguous_layout(rows: List[int], align: int = BLOCK) -> np.ndarray:
 
 
 def make_contiguous(rows: List[int], n: int, k: int, seed: int = 0, device="cpu",
-                    poison_padding: bool = False, ue8m0: bool = False) -> Contiguous:
+                    poison_padding: bool = False, ue8m0: bool = False, fp4: bool = False) -> Contiguous:
+    """fp4: B as packed E2M1 with per-32 power-of-two scales, and A's scales
+    powers of two too (the FP8 x FP4 GEMMs read every scale as UE8M0)."""
+    ue8m0 = ue8m0 or fp4
     layout_np = contiguous_layout(rows)
     m = int(layout_np.size)
     a, sfa = quantize_lhs(_randn((max(m, 1), k), seed, 1, device), ue8m0)
@@ -292,12 +345,13 @@ def make_contiguous(rows: List[int], n: int, k: int, seed: int = 0, device="cpu"
     if poison_padding and m:
         pad = layout < 0
         a.view(torch.uint8)[pad] = 0x7F  # E4M3 NaN
-    b, sfb = _quantize_rhs_grouped(len(rows), n, k, seed, device, ue8m0)
-    return Contiguous(a, sfa, b, sfb, layout, list(map(int, rows)), m, n, k, len(rows), ue8m0)
+    b, sfb = _quantize_rhs_grouped(len(rows), n, k, seed, device, ue8m0, fp4)
+    return Contiguous(a, sfa, b, sfb, layout, list(map(int, rows)), m, n, k, len(rows), ue8m0, fp4)
 
 
 def make_masked(counts: List[int], max_m: int, n: int, k: int, seed: int = 0, device="cpu",
-                poison_invalid: bool = False, ue8m0: bool = False) -> Masked:
+                poison_invalid: bool = False, ue8m0: bool = False, fp4: bool = False) -> Masked:
+    ue8m0 = ue8m0 or fp4
     num_groups = len(counts)
     a = torch.empty(num_groups, max_m, k, dtype=torch.float8_e4m3fn, device=device)
     sfa = torch.zeros(num_groups, k // BLOCK, tma_aligned_size(max_m), dtype=torch.float32, device=device)
@@ -308,9 +362,9 @@ def make_masked(counts: List[int], max_m: int, n: int, k: int, seed: int = 0, de
         if poison_invalid:
             valid = min(max(int(counts[g]), 0), max_m)
             a[g, valid:].view(torch.uint8).fill_(0x7F)
-    b, sfb = _quantize_rhs_grouped(num_groups, n, k, seed, device, ue8m0)
+    b, sfb = _quantize_rhs_grouped(num_groups, n, k, seed, device, ue8m0, fp4)
     masked_m = torch.tensor(list(counts), dtype=torch.int32, device=device)
-    return Masked(a, sfa, b, sfb, masked_m, list(map(int, counts)), max_m, n, k, num_groups, ue8m0)
+    return Masked(a, sfa, b, sfb, masked_m, list(map(int, counts)), max_m, n, k, num_groups, ue8m0, fp4)
 
 
 def make_nopad(rows: List[int], n: int, k: int, seed: int = 0, device="cpu", tail: int = 0,
@@ -386,7 +440,9 @@ def workload_spec(index: int, seed: int = 0) -> WorkloadSpec:
     the *_ue8m0 entry points;
     9 K-grouped weight gradient of workload 2's up projection: 8 groups with
       K = workload 2's row counts rounded up to 128, M = 4096 (output
-      features), N = 7168 (input features), accumulated into D in place.
+      features), N = 7168 (input features), accumulated into D in place;
+    10, 11: workloads 3 and 2 with B as packed E2M1 FP4 (per-32 scales), for
+      the FP8 x FP4 (W4A8) entry points.
     """
     if index == 0:
         return WorkloadSpec(0, "dense", "dense_128x256x512", n=256, k=512, m=128)
@@ -413,20 +469,25 @@ def workload_spec(index: int, seed: int = 0) -> WorkloadSpec:
         ks = [(r + BLOCK - 1) // BLOCK * BLOCK for r in rows]
         return WorkloadSpec(9, "k_grouped", "k_grouped_8x[3000,5000]_m4096_n7168", n=7168, k=int(sum(ks)), m=4096,
                             rows=ks)
+    if index in (10, 11):
+        base = workload_spec(3 if index == 10 else 2, seed)
+        return WorkloadSpec(index, base.kind, base.name.replace("_n", "_w4a8_n", 1), n=base.n, k=base.k, m=base.m,
+                            rows=base.rows, counts=base.counts, max_m=base.max_m, extra={"fp4": True})
     raise ValueError(f"no workload {index}")
 
 
-NUM_WORKLOADS = 10
+NUM_WORKLOADS = 12
 
 
 def make_workload(spec: WorkloadSpec, seed: int = 0, device="cpu"):
     e8 = bool(spec.extra.get("ue8m0", False))
+    fp4 = bool(spec.extra.get("fp4", False))
     if spec.kind == "dense":
         return make_dense(spec.m, spec.n, spec.k, seed, device, ue8m0=e8)
     if spec.kind == "contiguous":
-        return make_contiguous(spec.rows, spec.n, spec.k, seed, device, ue8m0=e8)
+        return make_contiguous(spec.rows, spec.n, spec.k, seed, device, ue8m0=e8, fp4=fp4)
     if spec.kind == "masked":
-        return make_masked(spec.counts, spec.max_m, spec.n, spec.k, seed, device, ue8m0=e8)
+        return make_masked(spec.counts, spec.max_m, spec.n, spec.k, seed, device, ue8m0=e8, fp4=fp4)
     if spec.kind == "nopad":
         return make_nopad(spec.rows, spec.n, spec.k, seed, device, ue8m0=e8)
     if spec.kind == "k_grouped":

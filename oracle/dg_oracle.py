@@ -32,7 +32,9 @@ Sources on the pages:
     (1, 128, 128) and the 128-row segment alignment; UE8M0 scale casting and
     the packed UE8M0 scale conversion (the *_ue8m0 variants below); the
     contiguous K-grouped FP8 NT GEMM with host K sizes, recipe (1, 1, 128)
-    and a float32 C (k_grouped_fp8_gemm_nt_contiguous below).
+    and a float32 C (k_grouped_fp8_gemm_nt_contiguous below); the FP8 x FP4
+    grouped GEMMs with FP8 E4M3 A, packed E2M1 B, LHS scales per 1x128 and
+    RHS scales per 1x32 (the *_fp8_fp4_* functions below).
 
 The 128-K block structure of the scales does not change the definition: the
 per-block sums scaled and added are algebraically the plain sum over the
@@ -63,6 +65,10 @@ design notes of the repository):
     and 128-wide K block for both operands (stored transposed like the LHS
     scales); C absent means zero; the result is float32 and is compared
     unrounded.
+  * FP8 x FP4 GEMMs: B holds OCP E2M1 values packed two per byte along K,
+    element 2j in the low nibble of byte j; its scales sfb[g][k // 32][n]
+    (one per row and 32-wide K block, stored transposed); all scales are read
+    as UE8M0 like the *_ue8m0 variants.
 """
 
 from __future__ import annotations
@@ -96,6 +102,13 @@ __all__ = [
     "k_grouped_ranges",
     "k_grouped_fp8_gemm_nt_contiguous",
     "k_grouped_f64_at",
+    "e2m1_value",
+    "e2m1_decode_table",
+    "unpack_e2m1",
+    "dequant_rhs_e2m1",
+    "m_grouped_fp8_fp4_gemm_nt_contiguous",
+    "m_grouped_fp8_fp4_gemm_nt_masked",
+    "fp8_fp4_f64_at",
 ]
 
 # Scale granularity along K for both operands: recipe (1, 128, 128).
@@ -454,3 +467,89 @@ def k_grouped_f64_at(a_codes, sfa, b_codes, sfb, ks, group, rows, cols, c_init=N
         val = c + ahat @ bhat.T
         mag = np.abs(c) + np.abs(ahat) @ np.abs(bhat).T
     return (val, mag) if abs_sum else val
+
+
+# ---------------------------------------------------------------------------
+# FP8 x FP4 (W4A8): packed E2M1 B with one scale per row and 32-wide K block
+# ---------------------------------------------------------------------------
+
+FP4_BLOCK_K = 32
+
+
+def e2m1_value(code: int) -> float:
+    """Value of one OCP E2M1 code (OCP Microscaling formats, FP4 E2M1): sign
+    bit 3, exponent bits 2..1 with bias 1, mantissa bit 0; exponent field 0
+    encodes subnormals (m/2 * 2^0). No infinity or NaN: 6 is the largest."""
+    sign = -1.0 if (code >> 3) & 1 else 1.0
+    e = (code >> 1) & 0x3
+    mant = code & 0x1
+    if e == 0:
+        return sign * mant * 0.5
+    return sign * (1.0 + mant / 2.0) * 2.0 ** (e - 1)
+
+
+def e2m1_decode_table() -> np.ndarray:
+    return np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def unpack_e2m1(packed) -> np.ndarray:
+    """E2M1 codes [..., 2 * L] from bytes [..., L]: element 2j is the low
+    nibble of byte j, element 2j + 1 its high nibble."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = packed & 0x0F
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+def dequant_rhs_e2m1(b_packed, sfb) -> np.ndarray:
+    """Bhat[n,k] = e2m1(B[n,k]) * E8M0(sfb[k // 32][n]); b_packed [N, K/2]."""
+    codes = unpack_e2m1(b_packed)
+    n, k = codes.shape
+    scale = e8m0_value(np.asarray(sfb)[:, :n]).T                 # [N, K/32]
+    assert scale.shape[1] * FP4_BLOCK_K == k
+    return e2m1_decode_table()[codes] * np.repeat(scale, FP4_BLOCK_K, axis=1)
+
+
+def m_grouped_fp8_fp4_gemm_nt_contiguous(a_codes, sfa, b_packed, sfb, layout, d_init) -> np.ndarray:
+    """Contiguous-layout FP8 x FP4 GEMM: as m_grouped_fp8_gemm_nt_contiguous
+    with Bhat_g from dequant_rhs_e2m1 and every scale read as E8M0.
+    b_packed [G, N, K/2], sfb [G, K/32, ld >= N]."""
+    layout = np.asarray(layout, dtype=np.int64)
+    d = np.array(d_init, dtype=np.uint16, copy=True)
+    sfa_v = e8m0_value(sfa)
+    for g in range(b_packed.shape[0]):
+        rows = np.nonzero(layout == g)[0]
+        if rows.size == 0:
+            continue
+        ahat = dequant_lhs(a_codes[rows], sfa_v[:, rows])
+        bhat = dequant_rhs_e2m1(b_packed[g], sfb[g])
+        d[rows] = bf16_bits(ahat @ bhat.T)
+    return d
+
+
+def m_grouped_fp8_fp4_gemm_nt_masked(a_codes, sfa, b_packed, sfb, masked_m, d_init) -> np.ndarray:
+    """Masked-layout FP8 x FP4 GEMM; a_codes [G, max_m, K], sfa [G, K/128, ld]."""
+    num_groups, max_m, _ = a_codes.shape
+    d = np.array(d_init, dtype=np.uint16, copy=True)
+    for g in range(num_groups):
+        valid = int(min(max(int(masked_m[g]), 0), max_m))
+        if valid == 0:
+            continue
+        ahat = dequant_lhs(a_codes[g, :valid], e8m0_value(sfa[g]))
+        bhat = dequant_rhs_e2m1(b_packed[g], sfb[g])
+        d[g, :valid] = bf16_bits(ahat @ bhat.T)
+    return d
+
+
+def fp8_fp4_f64_at(a_codes, sfa, b_packed_g, sfb_g, rows, cols) -> np.ndarray:
+    """Unrounded FP8 x FP4 result of one group at rows x cols: a_codes [M, K]
+    and sfa [K/128, ld] of that group's rows, b_packed_g [N, K/2],
+    sfb_g [K/32, ld]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    ahat = dequant_lhs(a_codes[rows], e8m0_value(sfa)[:, rows])
+    codes = unpack_e2m1(np.asarray(b_packed_g)[cols])
+    scale = e8m0_value(np.asarray(sfb_g))[:, cols].T
+    bhat = e2m1_decode_table()[codes] * np.repeat(scale, FP4_BLOCK_K, axis=1)
+    return ahat @ bhat.T

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = dg.lib()
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(n for n, _, _ in dg.SIGNATURES) == names
@@ -140,6 +140,26 @@ def test_ue8m0_variants_share_the_checks():
         assert call(a=None) == 1, name
         assert call(a=A + 8) == 3, name
         assert call(n=192) == 2, name
+
+
+def test_fp8_fp4_checks():
+    lib = dg.lib()
+    contig = lambda **kw: lib.dg_m_grouped_fp8_fp4_gemm_nt_contiguous(
+        kw.get("a", A), SFA, B, SFB, D, kw.get("lay", AUX), kw.get("m", 256), kw.get("n", 256), kw.get("k", 512),
+        2, None)
+    masked = lambda **kw: lib.dg_m_grouped_fp8_fp4_gemm_nt_masked(
+        kw.get("a", A), SFA, B, SFB, D, kw.get("lay", AUX), kw.get("g", 2), 64, kw.get("n", 256), kw.get("k", 512),
+        None)
+    for call in (contig, masked):
+        assert call(a=None) == 1
+        assert call(lay=None) == 1
+        assert call(a=A + 8) == 3
+        assert call(n=192) == 2
+        assert call(k=200) == 2
+    assert contig(m=130) == 2
+    assert contig(m=0) == 0
+    assert masked(g=4097) == 4
+    assert masked(g=0) == 0
 
 
 def test_k_grouped_checks():

@@ -455,6 +455,74 @@ def test_ue8m0_close_to_float32_path(dev):
 
 
 # ---------------------------------------------------------------------------
+# FP8 x FP4 (W4A8): packed E2M1 B, per-32 UE8M0 RHS scales
+# ---------------------------------------------------------------------------
+
+def _fp4_ref_rows(w, g, rows, cols, a=None, sfa=None):
+    a = NP(w.a) if a is None else a
+    sfa = NP(w.sfa) if sfa is None else sfa
+    return O.fp8_fp4_f64_at(a, sfa, NP(w.b)[g], NP(w.sfb)[g], rows, cols)
+
+
+@pytest.mark.parametrize("rows,n,k", [([130, 0, 77, 256, 1], 256, 512), ([5, 300, 1, 129], 384, 1024),
+                                      ([130, 0, 77, 256, 1], 896, 4096)])
+def test_fp8_fp4_contiguous_small(dev, rows, n, k):
+    _say(f"w4a8 contiguous rows={rows} n={n} k={k}")
+    w = synth.make_contiguous(rows, n, k, seed=len(rows) + 30, device=dev, poison_padding=True, fp4=True)
+    d = w.new_output()
+    dg.m_grouped_fp8_fp4_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout)
+    torch.cuda.synchronize()
+    got, layout = NP(d), NP(w.layout)
+    for g in range(w.num_groups):
+        idx = np.nonzero(layout == g)[0]
+        if idx.size:
+            check_close(got[idx], _fp4_ref_rows(w, g, idx, np.arange(w.n)), f"w4a8 contiguous group {g}")
+    check_untouched(got[layout < 0], "w4a8 contiguous padding rows")
+    ref_bits = O.m_grouped_fp8_fp4_gemm_nt_contiguous(NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb), layout,
+                                                      np.full((w.m, w.n), 0xFFFF, np.uint16))
+    assert np.all(ref_bits[layout < 0] == 0xFFFF)
+
+
+@pytest.mark.parametrize("counts,max_m,n,k", [([0, 1, 200, 77], 200, 256, 512), ([0, 1, 200, 77], 200, 896, 4096)])
+def test_fp8_fp4_masked_small(dev, counts, max_m, n, k):
+    _say(f"w4a8 masked counts={counts} n={n} k={k}")
+    w = synth.make_masked(counts, max_m, n, k, seed=max_m + 30, device=dev, poison_invalid=True, fp4=True)
+    d = w.new_output()
+    dg.m_grouped_fp8_fp4_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m)
+    torch.cuda.synchronize()
+    got = NP(d)
+    for g, c in enumerate(counts):
+        v = min(max(int(c), 0), max_m)
+        if v:
+            check_close(got[g, :v], _fp4_ref_rows(w, g, np.arange(v), np.arange(n), NP(w.a)[g], NP(w.sfa)[g]),
+                        f"w4a8 masked group {g}")
+        check_untouched(got[g, v:], f"w4a8 masked group {g} rows >= {v}")
+
+
+def test_fp8_fp4_integer_exact_bitwise(dev):
+    """A codes in {-2..2}, B any E2M1 value, scales 2^-1..2^1: every product
+    and partial sum is exact in float32, so the output matches bit for bit."""
+    rng = np.random.default_rng(73)
+    n, k = 384, 1024
+    m = 256
+    a8, sfa, _, _ = _int_exact(m, 128, k, seed=74)
+    sfa = np.ldexp(1.0, rng.integers(-1, 2, size=sfa.shape)).astype(np.float32)
+    codes = rng.integers(0, 16, size=(2, n, k)).astype(np.uint8)
+    b = (codes[:, :, 0::2] | (codes[:, :, 1::2] << 4)).astype(np.uint8)
+    sfb = np.zeros((2, k // 32, synth.tma_aligned_size(n)), np.float32)
+    sfb[:, :, :n] = np.ldexp(1.0, rng.integers(-1, 2, size=(2, k // 32, n)))
+    layout = np.r_[np.zeros(128), np.ones(100), np.full(28, -1)].astype(np.int32)  # 128-row aligned segments
+    d = synth.sentinel_output((m, n), dev)
+    dg.m_grouped_fp8_fp4_gemm_nt_contiguous(_dev_fp8(a8, dev), torch.from_numpy(sfa).to(dev),
+                                            torch.from_numpy(b).to(dev), torch.from_numpy(sfb).to(dev), d,
+                                            torch.from_numpy(layout).to(dev))
+    torch.cuda.synchronize()
+    ref = O.m_grouped_fp8_fp4_gemm_nt_contiguous(a8, sfa, b, sfb, layout, np.full((m, n), 0xFFFF, np.uint16))
+    got = NP(d)
+    assert np.array_equal(got, ref), f"{np.sum(got != ref)} mismatching elements"
+
+
+# ---------------------------------------------------------------------------
 # K-grouped GEMM (float32 output)
 # ---------------------------------------------------------------------------
 #
@@ -547,6 +615,25 @@ def test_workload_full_size(dev, index):
     dg.run_workload(w, d)
     torch.cuda.synchronize()
     rng = np.random.default_rng(100 + index)
+    if getattr(w, "fp4", False):
+        got = NP(d)
+        if spec.kind == "contiguous":
+            layout = NP(w.layout)
+            cols = _sample(w.n, 48, rng, (0, 127, 128, w.n - 1))
+            for g in range(w.num_groups):
+                idx = np.nonzero(layout == g)[0]
+                rows = idx[_sample(idx.size, 12, rng, (0, idx.size - 1))]
+                check_close(got[np.ix_(rows, cols)], _fp4_ref_rows(w, g, rows, cols), f"{spec.name} group {g}")
+            check_untouched(got[layout < 0], spec.name + " padding rows")
+        else:
+            for g in range(w.num_groups):
+                v = w.counts[g]
+                rows = _sample(v, 8, rng, (0, v - 1))
+                cols = _sample(w.n, 32, rng, (0, w.n - 1))
+                ref = _fp4_ref_rows(w, g, rows, cols, NP(w.a)[g], NP(w.sfa)[g])
+                check_close(got[g][np.ix_(rows, cols)], ref, f"{spec.name} group {g}")
+                check_untouched(got[g, v:], f"{spec.name} group {g} rows >= {v}")
+        return
     if spec.kind == "k_grouped":
         rows = _sample(w.m, 24, rng, (0, 255, 256, w.m - 1))
         cols = _sample(w.n, 24, rng, (0, 255, 256, w.n - 1))

@@ -104,6 +104,22 @@ def test_e8m0_golden_cases():
     check_e8m0_golden(O)
 
 
+def check_e2m1_golden(orc):
+    rows = _read_golden("e2m1_values.txt")
+    assert len(rows) == 16
+    table = orc.e2m1_decode_table()
+    for row in rows:
+        code_s, val_s = row.split()
+        code = int(code_s, 16)
+        expected = float(Fraction(val_s.lstrip("-"))) * (-1.0 if val_s.startswith("-") else 1.0)
+        assert table[code] == expected, (code_s, table[code])
+        assert math.copysign(1.0, table[code]) == math.copysign(1.0, expected), code_s
+
+
+def test_e2m1_golden_table():
+    check_e2m1_golden(O)
+
+
 def test_bf16_single_rounding_from_f64():
     # 1 + 2^-8 + 2^-40 is just above a tie; rounding through float32 first would
     # land exactly on the tie and then go down to 1.0

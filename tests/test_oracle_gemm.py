@@ -17,7 +17,10 @@ Each pin checks the oracle against something other than its own code:
     power-of-two scales, and math.frexp rounding down for other scales;
   * K-grouped GEMM: exact rationals with the indices written out, K-range
     splitting additivity, empty groups, and the dense GEMM as the special
-    case of one group with block-constant RHS scales.
+    case of one group with block-constant RHS scales;
+  * FP8 x FP4: a hand-derived E2M1 table (tests/golden/e2m1_values.txt), a
+    one-hot closed form fixing the packing order and the per-32 scale index,
+    exact rationals, and the FP8 UE8M0 GEMM on the same values re-encoded.
 
 test_planted_mistakes_are_caught plants plausible mistakes in a private copy
 of the oracle (wrong scale index, transposed RHS scales, wrong FP8 flavour,
@@ -41,6 +44,9 @@ from oracle import dg_oracle as O
 ORACLE_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "dg_oracle.py")
 
 CODE_OF = {0: 0x00, 1: 0x38, 2: 0x40, -1: 0xB8, -2: 0xC0}   # E4M3 codes of small integers
+# E4M3 codes of the E2M1 values (sign bit 7, exponent bias 7, 3 mantissa bits)
+CODE_OF_F = {0.0: 0x00, 0.5: 0x30, 1.0: 0x38, 1.5: 0x3C, 2.0: 0x40, 3.0: 0x44, 4.0: 0x48, 6.0: 0x4C,
+             -0.5: 0xB0, -1.0: 0xB8, -1.5: 0xBC, -2.0: 0xC0, -3.0: 0xC4, -4.0: 0xC8, -6.0: 0xCC}
 
 
 # ---------------------------------------------------------------------------
@@ -438,6 +444,96 @@ def pin_k_grouped_invariants(orc):
     np.testing.assert_allclose(one, orc.gemm_nt_f64(a, sfa, b, blocks), rtol=1e-12, atol=1e-9)
 
 
+E2M1_OF = {0.0: 0x0, 0.5: 0x1, 1.0: 0x2, 1.5: 0x3, 2.0: 0x4, 3.0: 0x5, 4.0: 0x6, 6.0: 0x7}
+
+
+def _pack_e2m1(values):
+    """Pack E2M1 values [N, K] two per byte, element 2j in the low nibble of byte j."""
+    codes = np.vectorize(lambda v: E2M1_OF[abs(v)] | (0x8 if v < 0 else 0))(values).astype(np.uint8)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def pin_e2m1_golden(orc):
+    import test_oracle_formats as F
+    F.check_e2m1_golden(orc)
+
+
+def pin_fp4_element_positions(orc):
+    """One nonzero E2M1 element per B row, at K position k_n (odd and even
+    positions, in different 32-K scale blocks): D[m][n] = A[m][k_n] *
+    sa * sb, a closed form that fixes the packing order and the scale index."""
+    rng = np.random.default_rng(61)
+    k, n, rows = 256, 128, 8
+    vals_a = rng.integers(-2, 3, size=(rows, k))
+    a = np.vectorize(CODE_OF.get)(vals_a).astype(np.uint8)
+    pos = rng.integers(0, k, size=n)
+    bvals = np.zeros((n, k))
+    bvals[np.arange(n), pos] = 1.5
+    b = _pack_e2m1(bvals)[None]
+    sfa = np.ldexp(1.0, rng.integers(-3, 3, size=(k // 128, rows))).astype(np.float32)
+    e_b = rng.integers(-3, 3, size=(k // 32, n))
+    sfb = np.ldexp(1.0, e_b).astype(np.float32)[None]
+    layout = np.zeros(rows, np.int32)
+    a_pad = np.concatenate([a, np.zeros((128 - rows, k), np.uint8)])
+    lay_pad = np.r_[layout, np.full(128 - rows, -1)].astype(np.int32)
+    sfa_pad = np.pad(sfa, ((0, 0), (0, 128 - rows)))
+    d = orc.m_grouped_fp8_fp4_gemm_nt_contiguous(a_pad, sfa_pad, b, sfb, lay_pad,
+                                                 np.full((128, n), 0xFFFF, np.uint16))
+    got = O.bf16_bits_to_f64(d[:rows])
+    for i in range(rows):
+        for j in range(n):
+            kk = int(pos[j])
+            expect = vals_a[i, kk] * 1.5 * float(sfa[kk // 128, i]) * 2.0 ** int(e_b[kk // 32, j])
+            assert got[i, j] == expect, (i, j, kk)
+
+
+def pin_exact_fp8_fp4(orc):
+    """A tiny masked FP8 x FP4 case against exact rationals (values from a
+    hand-written E2M1 table, scales 2^e)."""
+    rng = np.random.default_rng(67)
+    g_count, max_m, n, k = 2, 3, 128, 256
+    a, _, _, _ = _random_inputs(rng, g_count * max_m, n, k)
+    a = a.reshape(g_count, max_m, k)
+    grid = np.array(sorted(E2M1_OF))
+    bvals = rng.choice(grid, size=(g_count, n, k)) * rng.choice([-1.0, 1.0], size=(g_count, n, k))
+    b = np.stack([_pack_e2m1(bvals[g]) for g in range(g_count)])
+    ea = rng.integers(-4, 4, size=(g_count, k // 128, 4))
+    eb = rng.integers(-4, 4, size=(g_count, k // 32, n))
+    sfa, sfb = np.ldexp(1.0, ea).astype(np.float32), np.ldexp(1.0, eb).astype(np.float32)
+    masked = np.array([3, 2], np.int32)
+    d = orc.m_grouped_fp8_fp4_gemm_nt_masked(a, sfa, b, sfb, masked, np.full((g_count, max_m, n), 0xFFFF, np.uint16))
+    av = _decode_torch(a.reshape(-1, k)).reshape(g_count, max_m, k)
+    for g in range(g_count):
+        for i in range(masked[g]):
+            for j in range(0, n, 7):
+                ex = sum(Fraction(float(av[g, i, kk])) * Fraction(2) ** int(ea[g, kk // 128, i])
+                         * Fraction(float(bvals[g, j, kk])) * Fraction(2) ** int(eb[g, kk // 32, j])
+                         for kk in range(k))
+                assert int(d[g, i, j]) == _bf16_rne_exact(ex), (g, i, j)
+    assert np.all(d[1, 2:] == 0xFFFF)
+
+
+def pin_fp4_matches_fp8_on_shared_values(orc):
+    """Every E2M1 value is an E4M3 value: with RHS scales constant over
+    128 x 128 blocks, the FP8 x FP4 GEMM equals the FP8 UE8M0 GEMM on the same
+    values re-encoded as E4M3."""
+    rng = np.random.default_rng(71)
+    n, k, m_rows = 256, 256, 128
+    a, _, _, _ = _random_inputs(rng, m_rows, n, k)
+    grid = np.array(sorted(E2M1_OF))
+    bvals = rng.choice(grid, size=(n, k)) * rng.choice([-1.0, 1.0], size=(n, k))
+    b4 = _pack_e2m1(bvals)[None]
+    b8 = np.vectorize(lambda v: CODE_OF_F[v])(bvals).astype(np.uint8)[None]
+    eblk = rng.integers(-3, 3, size=(n // 128, k // 128))
+    sfb8 = np.ldexp(1.0, eblk).astype(np.float32)[None]
+    sfb4 = np.ldexp(1.0, np.repeat(np.repeat(eblk.T, 4, axis=0), 128, axis=1)).astype(np.float32)[None]
+    sfa = np.ldexp(1.0, rng.integers(-3, 3, size=(k // 128, m_rows))).astype(np.float32)
+    layout = np.zeros(m_rows, np.int32)
+    d0 = np.full((m_rows, n), 0xFFFF, np.uint16)
+    assert np.array_equal(orc.m_grouped_fp8_fp4_gemm_nt_contiguous(a, sfa, b4, sfb4, layout, d0),
+                          orc.m_grouped_fp8_gemm_nt_contiguous_ue8m0(a, sfa, b8, sfb8, layout, d0))
+
+
 def pin_contiguous_poisoned_padding(orc):
     rng = np.random.default_rng(17)
     rows = [5, 128, 1]
@@ -506,6 +602,10 @@ PINS = [
     pin_ue8m0_drops_mantissa,
     pin_exact_k_grouped,
     pin_k_grouped_invariants,
+    pin_e2m1_golden,
+    pin_fp4_element_positions,
+    pin_exact_fp8_fp4,
+    pin_fp4_matches_fp8_on_shared_values,
 ]
 
 
@@ -699,6 +799,33 @@ def _mut_k_grouped_drops_c(mod):
     mod.k_grouped_fp8_gemm_nt_contiguous = f
 
 
+def _mut_e2m1_nibbles_swapped(mod):
+    def f(packed):
+        packed = np.asarray(packed, dtype=np.uint8)
+        out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.uint8)
+        out[..., 0::2] = packed >> 4
+        out[..., 1::2] = packed & 0x0F
+        return out
+    mod.unpack_e2m1 = f
+
+
+def _mut_fp4_scale_per_128(mod):
+    # the RHS scale of the first 32-K block of each 128-K block for all four
+    orig = mod.dequant_rhs_e2m1
+
+    def f(b_packed, sfb):
+        s = np.array(sfb, copy=True)
+        s[:] = np.repeat(s[0::4], 4, axis=0)[:s.shape[0]]
+        return orig(b_packed, s)
+    mod.dequant_rhs_e2m1 = f
+
+
+def _mut_e2m1_bias_0(mod):
+    def table():
+        return np.array([mod.e2m1_value(c) * (2.0 if (c >> 1) & 3 else 1.0) for c in range(16)])
+    mod.e2m1_decode_table = table
+
+
 MUTANTS = [
     _mut_lhs_scale_first_row,
     _mut_rhs_scale_transposed,
@@ -719,6 +846,9 @@ MUTANTS = [
     _mut_k_grouped_restart,
     _mut_k_grouped_rhs_block_scales,
     _mut_k_grouped_drops_c,
+    _mut_e2m1_nibbles_swapped,
+    _mut_fp4_scale_per_128,
+    _mut_e2m1_bias_0,
 ]
 
 
