@@ -164,17 +164,23 @@ __global__ void __launch_bounds__(Cfg::THREADS, 1) fp8_fp4_gemm_kernel(GemmArgs 
 
   const uint32_t base = lds_addr();
   const uint8_t* const buf = lds();
+  // The first K block of each tile is loaded during the previous tile's last
+  // K step, so that its loads overlap that tile's epilogue.
   int t = rank;
-  while (true) {
-    const TileRef cur = next_active<Cfg, KIND>(p, t, grid, num_tiles, s_prefix);
-    if (!cur.active) break;
+  TileRef cur = next_active<Cfg, KIND>(p, t, grid, num_tiles, s_prefix);
+  Src src = tile_src(p, cur);
+  int stage = 0;  // the stage holding the current tile's first K block
+  if (cur.active) issue_block(p, src, 0, base, wave, lane, a_lane_off);
+  while (cur.active) {
+    int tn = t + grid;
+    const TileRef nxt = next_active<Cfg, KIND>(p, tn, grid, num_tiles, s_prefix);
+    const Src nsrc = nxt.active ? tile_src(p, nxt) : src;
     RowMask cm{0, 0};
     if constexpr (KIND == KIND_CONTIGUOUS) cm = row_mask(load_row_groups<Cfg>(p, cur, wm0, lane), cur.group);
     bool any_row;
     if constexpr (KIND == KIND_CONTIGUOUS) any_row = (cm.even | cm.odd) != 0;
     else any_row = cur.valid_rows > cur.m0 + wm0;
     const bool on = any_row && cur.n0 + wn0 < p.n;
-    const Src src = tile_src(p, cur);
 
     f32x4 acc[Cfg::MT][Cfg::NT];
 #pragma unroll
@@ -182,13 +188,19 @@ __global__ void __launch_bounds__(Cfg::THREADS, 1) fp8_fp4_gemm_kernel(GemmArgs 
 #pragma unroll
       for (int nt = 0; nt < Cfg::NT; ++nt) acc[mt][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    __syncthreads();  // no wave still reads the previous tile's stages
-    issue_block(p, src, 0, base, wave, lane, a_lane_off);
     for (int i = 0; i < k_blocks; ++i) {
-      __syncthreads();  // block i has landed everywhere; nobody reads the other stage
-      if (i + 1 < k_blocks) issue_block(p, src, i + 1, base + ((i + 1) & 1) * STAGE_BYTES, wave, lane, a_lane_off);
-      if (on) block(acc, buf + (i & 1) * STAGE_BYTES, wm0, wn0, lane);
+      const int cs = (stage + i) & 1;
+      // Block i has landed for every wave (each waits for all its loads and
+      // stores, then all meet), and nobody reads the other stage any more.
+      // The wait is explicit: the compiler does not see the direct-to-LDS
+      // loads (bare LDS addresses), and its barrier waits only for what it sees.
+      wait_vmcnt_0();
+      __syncthreads();
+      if (i + 1 < k_blocks) issue_block(p, src, i + 1, base + (cs ^ 1) * STAGE_BYTES, wave, lane, a_lane_off);
+      else if (nxt.active) issue_block(p, nsrc, 0, base + (cs ^ 1) * STAGE_BYTES, wave, lane, a_lane_off);
+      if (on) block(acc, buf + cs * STAGE_BYTES, wm0, wn0, lane);
     }
+    stage = (stage + k_blocks) & 1;
 
     if (on) {
 #pragma unroll
@@ -204,7 +216,9 @@ __global__ void __launch_bounds__(Cfg::THREADS, 1) fp8_fp4_gemm_kernel(GemmArgs 
         }
       }
     }
-    t += grid;
+    cur = nxt;
+    src = nsrc;
+    t = tn;
   }
   wait_vmcnt_0();
 }

@@ -163,8 +163,17 @@ __global__ void __launch_bounds__(THREADS, 1) k_grouped_kernel(KGroupedArgs p) {
 
   const uint32_t base = lds_addr();
   const uint8_t* const buf = lds();
-  for (int t = rank; t < p.num_tiles; t += grid) {
+  // The first K block of a tile is loaded during the previous tile's last K
+  // step when there is one (a tile of an empty group has no K step: the next
+  // tile then loads its own first block).
+  int t = rank;
+  int stage = 0;        // the stage that holds (or will hold) the current tile's first block
+  bool loaded = false;  // whether the current tile's first block has been issued
+  while (t < p.num_tiles) {
     const Tile tl = tile_at(p, t);
+    const int tn = t + grid;
+    const bool has_next = tn < p.num_tiles;
+    const Tile nx = has_next ? tile_at(p, tn) : tl;
     const bool on = tl.m0 + wm0 < p.m && tl.n0 + wn0 < p.n;
     f32x4 acc[MT][NT];
 #pragma unroll
@@ -172,17 +181,30 @@ __global__ void __launch_bounds__(THREADS, 1) k_grouped_kernel(KGroupedArgs p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // No wave still reads the previous tile's stages.
-    __syncthreads();
-    if (tl.nkb > 0) issue_block(p, tl, tl.kb0, base, wave, lane, lane_off);
-    for (int i = 0; i < tl.nkb; ++i) {
-      // Block i has landed for every wave (each waits for its own loads,
-      // then all meet), and nobody reads the other stage any more.
-      __syncthreads();
-      if (i + 1 < tl.nkb)
-        issue_block(p, tl, tl.kb0 + i + 1, base + ((i + 1) & 1) * STAGE_BYTES, wave, lane, lane_off);
-      if (on) block(acc, buf + (i & 1) * STAGE_BYTES, o);
+    if (tl.nkb > 0 && !loaded) {
+      wait_vmcnt_0();
+      __syncthreads();  // no wave still reads the stage
+      issue_block(p, tl, tl.kb0, base + stage * STAGE_BYTES, wave, lane, lane_off);
     }
+    bool next_loaded = false;
+    for (int i = 0; i < tl.nkb; ++i) {
+      const int cs = (stage + i) & 1;
+      // Block i has landed for every wave (each waits for its own loads,
+      // then all meet), and nobody reads the other stage any more. The
+      // wait is explicit: the compiler does not see the direct-to-LDS loads
+      // (bare LDS addresses), and its barrier waits only for what it sees.
+      wait_vmcnt_0();
+      __syncthreads();
+      if (i + 1 < tl.nkb) {
+        issue_block(p, tl, tl.kb0 + i + 1, base + (cs ^ 1) * STAGE_BYTES, wave, lane, lane_off);
+      } else if (has_next && nx.nkb > 0) {
+        issue_block(p, nx, nx.kb0, base + (cs ^ 1) * STAGE_BYTES, wave, lane, lane_off);
+        next_loaded = true;
+      }
+      if (on) block(acc, buf + cs * STAGE_BYTES, o);
+    }
+    stage = (stage + tl.nkb) & 1;
+    loaded = next_loaded;
 
     if (on) {
 #pragma unroll
@@ -198,6 +220,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_grouped_kernel(KGroupedArgs p) {
         }
       }
     }
+    t = tn;
   }
   // Loads issued past the last block read: none (every issued block is read).
   wait_vmcnt_0();
