@@ -32,7 +32,8 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 HEADLINE = 1                 # dense 4096x7168x2048
 # The device code of the kernels (the traffic figures are valid for it only).
 KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_gemm_amd", "csrc", f)
-                  for f in ("dg_device.h", "dg_kernel.hip", "dg_kernel_deep.hip", "dg_kernel_kgrouped.hip")]
+                  for f in ("dg_device.h", "dg_kernel.hip", "dg_kernel_deep.hip", "dg_kernel_kgrouped.hip",
+                            "dg_kernel_fp4.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -191,7 +192,8 @@ def main():
                    "accumulate": "fp32 with per-128-K promotion", "output": "bf16", "seed": 0},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "k_grouped_kernel" if spec.kind == "k_grouped" else "fp8_gemm_nt_kernel",
+                     "kernel": ("k_grouped_kernel" if spec.kind == "k_grouped" else
+                                "fp8_fp4_gemm_kernel" if spec.extra.get("fp4") else "fp8_gemm_nt_kernel"),
                      "kernel_ms": round(kernel_ms, 5),
                      "algorithmic_bytes": w.algorithmic_bytes()},
     }
