@@ -230,6 +230,17 @@ dg_status dg_k_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa,
                                               const int* ks, int num_groups,
                                               int m, int n, void* stream);
 
+/* The K-grouped GEMM with power-of-two scales applied by the matrix cores:
+ * arguments and checks as above, every scale read as UE8M0 exactly as by
+ * the other *_ue8m0 calls (2^(e - 127), e the float32 exponent field). The
+ * per-row scales of both operands become the MFMA's per-lane E8M0 block
+ * scales, and the products accumulate in the MFMA: no promotion step. */
+dg_status dg_k_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* a, const float* sfa,
+                                                    const void* b, const float* sfb,
+                                                    const float* c, float* d,
+                                                    const int* ks, int num_groups,
+                                                    int m, int n, void* stream);
+
 /* Row alignment of each group's segment in the contiguous layout: 128
  * ("DeepGEMM Compatibility Wrapper" page, "Contiguous Grouped GEMM
  * Alignment"; "DeepGEMM for PPU" README, "Utilities"). */

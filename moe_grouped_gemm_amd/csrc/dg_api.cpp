@@ -265,9 +265,12 @@ dg_status dg_m_grouped_fp8_fp4_gemm_nt_masked(const void* a, const float* sfa, c
              : DG_ERR_LAUNCH;
 }
 
-dg_status dg_k_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, const void* b, const float* sfb,
-                                              const float* c, float* d, const int* ks, int num_groups, int m, int n,
-                                              void* stream) {
+}  // extern "C"
+
+namespace {
+
+dg_status k_grouped(const void* a, const float* sfa, const void* b, const float* sfb, const float* c, float* d,
+                    const int* ks, int num_groups, int m, int n, bool e8m0, void* stream) {
   if (!a || !sfa || !b || !sfb || !d || !ks) return DG_ERR_NULL;
   if (num_groups <= 0 || m < 0 || n <= 0 || n % 128 != 0) return DG_ERR_SHAPE;
   if (num_groups > dg::MAX_KGROUPED_GROUPS) return DG_ERR_UNSUPPORTED;
@@ -298,6 +301,7 @@ dg_status dg_k_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, c
   args.num_groups = num_groups;
   args.ld_sfa = tma_aligned(m, 4);
   args.ld_sfb = tma_aligned(n, 4);
+  args.scale_e8m0 = e8m0 ? 1 : 0;
   int off = 0;
   for (int g = 0; g < num_groups; ++g) {
     args.k_off[g] = off;
@@ -308,6 +312,22 @@ dg_status dg_k_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, c
   if (cus <= 0) return DG_ERR_DEVICE;
   return dg::launch_k_grouped(args, cus, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? DG_OK
                                                                                                 : DG_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_k_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, const void* b, const float* sfb,
+                                              const float* c, float* d, const int* ks, int num_groups, int m, int n,
+                                              void* stream) {
+  return k_grouped(a, sfa, b, sfb, c, d, ks, num_groups, m, n, false, stream);
+}
+
+dg_status dg_k_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* a, const float* sfa, const void* b,
+                                                    const float* sfb, const float* c, float* d, const int* ks,
+                                                    int num_groups, int m, int n, void* stream) {
+  return k_grouped(a, sfa, b, sfb, c, d, ks, num_groups, m, n, true, stream);
 }
 
 int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }

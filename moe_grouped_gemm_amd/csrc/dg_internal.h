@@ -57,6 +57,7 @@ struct KGroupedArgs {
   int m, n, k;         // k: the total K, also the row stride of A and B
   int num_groups;
   int ld_sfa, ld_sfb;
+  int scale_e8m0;                          // nonzero: scales read as E8M0 and applied by the MFMA
   int m_blocks, n_blocks, num_tiles;       // filled in by launch_k_grouped
   int k_off[MAX_KGROUPED_GROUPS + 1];      // first K block of each group; k_off[G] = k / 128
 };

@@ -108,18 +108,26 @@ __device__ __forceinline__ void issue_block(const KGroupedArgs& p, const Tile& t
 // columns' RHS scales.
 struct Offsets {
   uint32_t a0, a1, b0, b1, sa, sb;
+  uint32_t sb_row;  // the RHS scale of the B row this lane holds in the MFMA operand
 };
 
 // One K block of a wave's 128 x 64 sub-tile from the stage at `st`.
+// Float32 scales: partial sums promoted with each column's own RHS scale.
+// Power-of-two scales (E8): the MFMA applies them as E8M0 codes, one per
+// lane and operand (the B operand's lane holds row lane % 16 of its 16-row
+// block, the A operand's likewise), and accumulates into the totals.
+template <bool E8>
 __device__ __forceinline__ void block(f32x4 (&acc)[MT][NT], const uint8_t* st, const Offsets& o) {
   i32x8 bf[NT];
-  f32x4 sb[NT];
+  [[maybe_unused]] f32x4 sb[NT];
+  [[maybe_unused]] int eb[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const i32x4 x = *reinterpret_cast<const i32x4*>(st + o.b0 + nt * 16 * ROW_BYTES);
     const i32x4 y = *reinterpret_cast<const i32x4*>(st + o.b1 + nt * 16 * ROW_BYTES);
     bf[nt] = (i32x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-    sb[nt] = *reinterpret_cast<const f32x4*>(st + o.sb + nt * 64);
+    if constexpr (E8) eb[nt] = e8m0_code(*reinterpret_cast<const float*>(st + o.sb_row + nt * 64));
+    else sb[nt] = *reinterpret_cast<const f32x4*>(st + o.sb + nt * 64);
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -129,14 +137,19 @@ __device__ __forceinline__ void block(f32x4 (&acc)[MT][NT], const uint8_t* st, c
     const float sa = *reinterpret_cast<const float*>(st + o.sa + mt * 64);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const f32x4 part =
-          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-      acc[mt][nt] += part * (sb[nt] * sa);
+      if constexpr (E8) {
+        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af, acc[mt][nt], 0, 0, 0, eb[nt], 0,
+                                                                      e8m0_code(sa));
+      } else {
+        const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af, (f32x4){0.f, 0.f, 0.f, 0.f},
+                                                                           0, 0, 0, 0, 0, 0);
+        acc[mt][nt] += part * (sb[nt] * sa);
+      }
     }
   }
 }
 
-template <bool HAS_C>
+template <bool HAS_C, bool E8>
 __global__ void __launch_bounds__(THREADS, 1) k_grouped_kernel(KGroupedArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -155,6 +168,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_grouped_kernel(KGroupedArgs p) {
   o.b1 = (uint32_t)(A_BYTES + wn0 * ROW_BYTES + lds_offset(r, q + 4));
   o.sa = (uint32_t)(SA_OFF + 4 * (wm0 + r));
   o.sb = (uint32_t)(SB_OFF + 4 * (wn0 + 4 * q));
+  o.sb_row = (uint32_t)(SB_OFF + 4 * (wn0 + r));
 
   // XCD-aware rank, as in the other kernels.
   const int grid = gridDim.x;
@@ -201,7 +215,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_grouped_kernel(KGroupedArgs p) {
         issue_block(p, nx, nx.kb0, base + (cs ^ 1) * STAGE_BYTES, wave, lane, lane_off);
         next_loaded = true;
       }
-      if (on) block(acc, buf + cs * STAGE_BYTES, o);
+      if (on) block<E8>(acc, buf + cs * STAGE_BYTES, o);
     }
     stage = (stage + tl.nkb) & 1;
     loaded = next_loaded;
@@ -233,7 +247,8 @@ hipError_t launch_k_grouped(KGroupedArgs& args, int num_cus, hipStream_t stream)
   args.m_blocks = (args.m + BM - 1) / BM;
   args.n_blocks = (args.n + BN - 1) / BN;
   args.num_tiles = args.num_groups * args.m_blocks * args.n_blocks;
-  auto kern = args.c ? k_grouped_kernel<true> : k_grouped_kernel<false>;
+  auto kern = args.scale_e8m0 ? (args.c ? k_grouped_kernel<true, true> : k_grouped_kernel<false, true>)
+                              : (args.c ? k_grouped_kernel<true, false> : k_grouped_kernel<false, false>);
   int per_cu = 1;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, THREADS, 0);
   if (e != hipSuccess) return e;

@@ -35,6 +35,8 @@ SIGNATURES = [
     ("dg_m_grouped_fp8_fp4_gemm_nt_contiguous", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     ("dg_m_grouped_fp8_fp4_gemm_nt_masked", [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     ("dg_k_grouped_fp8_gemm_nt_contiguous", [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_i), _i, _i, _i, _vp], _i),
+    ("dg_k_grouped_fp8_gemm_nt_contiguous_ue8m0", [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_i), _i, _i, _i, _vp],
+     _i),
     ("dg_get_mk_alignment_for_contiguous_layout", [], _i),
     ("dg_get_tma_aligned_size", [_i, _i], _i),
     ("dg_get_num_cus", [], _i),
@@ -278,13 +280,14 @@ def m_grouped_fp8_fp4_gemm_nt_masked(a, sfa, b, sfb, d, masked_m) -> torch.Tenso
     return d
 
 
-def k_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, ks, c=None) -> torch.Tensor:
+def k_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, ks, c=None, ue8m0: bool = False) -> torch.Tensor:
     """K-grouped GEMM (weight-gradient shape): for each group g,
     d[g] = (c[g] or 0) + A[:, K_g] . B[:, K_g]^T with per-row, per-128-K
     scales on both operands. a [M, K], sfa [K/128, tma_aligned(M)],
     b [N, K], sfb [K/128, tma_aligned(N)], d [G, M, N] float32; ks: the
     groups' K sizes as host integers (multiples of 128, summing to K);
-    c: None, d itself (accumulate in place) or a separate [G, M, N] float32."""
+    c: None, d itself (accumulate in place) or a separate [G, M, N] float32.
+    ue8m0=True: power-of-two scales applied by the matrix cores."""
     dev = a.device
     m, k = a.shape
     n = b.shape[0]
@@ -305,7 +308,7 @@ def k_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, d, ks, c=None) -> torch.Ten
             or tuple(sfb.shape) != (k // 128, get_tma_aligned_size(n, 4))):
         raise ValueError("scale shapes do not match the (1, 1, 128) recipe layout")
     ks_arr = (ctypes.c_int * max(g, 1))(*ks)
-    _check(lib().dg_k_grouped_fp8_gemm_nt_contiguous(
+    _check(_entry("dg_k_grouped_fp8_gemm_nt_contiguous", ue8m0)(
         a.data_ptr(), sfa.data_ptr(), b.data_ptr(), sfb.data_ptr(), None if c is None else c.data_ptr(),
         d.data_ptr(), ks_arr, g, m, n, _stream(a)), "dg_k_grouped_fp8_gemm_nt_contiguous")
     return d
@@ -330,5 +333,5 @@ def run_workload(w, d: torch.Tensor) -> torch.Tensor:
         return m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows, ue8m0=e8)
     if kind == "KGrouped":
         # the weight-gradient use: accumulate into d in place
-        return k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.ks, c=d)
+        return k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.ks, c=d, ue8m0=e8)
     raise TypeError(kind)

@@ -289,6 +289,7 @@ class KGrouped:
     k: int
     num_groups: int
     seed: int = 0
+    ue8m0: bool = False
 
     def new_output(self) -> torch.Tensor:
         """A float32 [G, M, N] accumulator with seeded N(0, 1) starting values."""
@@ -385,17 +386,17 @@ def make_nopad(rows: List[int], n: int, k: int, seed: int = 0, device="cpu", tai
     return w
 
 
-def make_k_grouped(ks: List[int], m: int, n: int, seed: int = 0, device="cpu") -> KGrouped:
+def make_k_grouped(ks: List[int], m: int, n: int, seed: int = 0, device="cpu", ue8m0: bool = False) -> KGrouped:
     """K-grouped operands: A [M, K] and B [N, K] with one scale per row and
     128-wide K block for both (recipe (1, 1, 128)): each is quantised like
     the LHS of the other GEMMs."""
     k = int(sum(ks))
     assert all(x % BLOCK == 0 and x >= 0 for x in ks)
-    a, sfa = quantize_lhs(_randn((m, max(k, BLOCK)), seed, 11, device))
-    b, sfb = quantize_lhs(_randn((n, max(k, BLOCK)), seed, 12, device))
+    a, sfa = quantize_lhs(_randn((m, max(k, BLOCK)), seed, 11, device), ue8m0)
+    b, sfb = quantize_lhs(_randn((n, max(k, BLOCK)), seed, 12, device), ue8m0)
     a, b = a[:, :k].contiguous(), b[:, :k].contiguous()
     sfa, sfb = sfa[:k // BLOCK].contiguous(), sfb[:k // BLOCK].contiguous()
-    return KGrouped(a, sfa, b, sfb, list(map(int, ks)), m, n, k, len(ks), seed)
+    return KGrouped(a, sfa, b, sfb, list(map(int, ks)), m, n, k, len(ks), seed, ue8m0)
 
 
 # ---------------------------------------------------------------------------
@@ -442,7 +443,8 @@ def workload_spec(index: int, seed: int = 0) -> WorkloadSpec:
       K = workload 2's row counts rounded up to 128, M = 4096 (output
       features), N = 7168 (input features), accumulated into D in place;
     10, 11: workloads 3 and 2 with B as packed E2M1 FP4 (per-32 scales), for
-      the FP8 x FP4 (W4A8) entry points.
+      the FP8 x FP4 (W4A8) entry points;
+    12: workload 9 with power-of-two scales, for the K-grouped *_ue8m0 call.
     """
     if index == 0:
         return WorkloadSpec(0, "dense", "dense_128x256x512", n=256, k=512, m=128)
@@ -473,10 +475,14 @@ def workload_spec(index: int, seed: int = 0) -> WorkloadSpec:
         base = workload_spec(3 if index == 10 else 2, seed)
         return WorkloadSpec(index, base.kind, base.name.replace("_n", "_w4a8_n", 1), n=base.n, k=base.k, m=base.m,
                             rows=base.rows, counts=base.counts, max_m=base.max_m, extra={"fp4": True})
+    if index == 12:
+        base = workload_spec(9, seed)
+        return WorkloadSpec(12, base.kind, base.name + "_ue8m0", n=base.n, k=base.k, m=base.m, rows=base.rows,
+                            extra={"ue8m0": True})
     raise ValueError(f"no workload {index}")
 
 
-NUM_WORKLOADS = 12
+NUM_WORKLOADS = 13
 
 
 def make_workload(spec: WorkloadSpec, seed: int = 0, device="cpu"):
@@ -491,7 +497,7 @@ def make_workload(spec: WorkloadSpec, seed: int = 0, device="cpu"):
     if spec.kind == "nopad":
         return make_nopad(spec.rows, spec.n, spec.k, seed, device, ue8m0=e8)
     if spec.kind == "k_grouped":
-        return make_k_grouped(spec.rows, spec.m, spec.n, seed, device)
+        return make_k_grouped(spec.rows, spec.m, spec.n, seed, device, ue8m0=e8)
     raise ValueError(spec.kind)
 
 

@@ -102,6 +102,7 @@ __all__ = [
     "k_grouped_ranges",
     "k_grouped_fp8_gemm_nt_contiguous",
     "k_grouped_f64_at",
+    "k_grouped_fp8_gemm_nt_contiguous_ue8m0",
     "e2m1_value",
     "e2m1_decode_table",
     "unpack_e2m1",
@@ -450,6 +451,11 @@ def k_grouped_fp8_gemm_nt_contiguous(a_codes, sfa, b_codes, sfb, ks, c_init=None
             ahat, bhat = _k_group_operands(a_codes, sfa, b_codes, sfb, k0, k1)
             d[g] += ahat @ bhat.T
     return d
+
+
+def k_grouped_fp8_gemm_nt_contiguous_ue8m0(a_codes, sfa, b_codes, sfb, ks, c_init=None) -> np.ndarray:
+    """The K-grouped GEMM with every scale taken as its E8M0 value."""
+    return k_grouped_fp8_gemm_nt_contiguous(a_codes, e8m0_value(sfa), b_codes, e8m0_value(sfb), ks, c_init)
 
 
 def k_grouped_f64_at(a_codes, sfa, b_codes, sfb, ks, group, rows, cols, c_init=None, abs_sum=False):

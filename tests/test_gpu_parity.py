@@ -543,6 +543,8 @@ def _check_k_grouped(w, d, c0, what, groups=None, rows=None, cols=None):
     rows = np.arange(w.m) if rows is None else rows
     cols = np.arange(w.n) if cols is None else cols
     a, sfa, b, sfb = NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb)
+    if w.ue8m0:
+        sfa, sfb = O.e8m0_value(sfa), O.e8m0_value(sfb)
     for g in (range(w.num_groups) if groups is None else groups):
         ref, mag = O.k_grouped_f64_at(a, sfa, b, sfb, w.ks, g, rows, cols, c_np, abs_sum=True)
         cmag = 0.0 if c_np is None else np.abs(c_np[g][np.ix_(rows, cols)])
@@ -581,6 +583,18 @@ def test_k_grouped_small(dev, ks, m, n, c_mode):
         dg.k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.ks, c=d)
     torch.cuda.synchronize()
     _check_k_grouped(w, d, c0, f"k_grouped {ks} {c_mode}")
+
+
+@pytest.mark.parametrize("ks,m,n", [([128, 0, 384, 256], 300, 384), ([4096], 130, 256)])
+def test_k_grouped_ue8m0(dev, ks, m, n):
+    _say(f"k_grouped ue8m0 ks={ks} m={m} n={n}")
+    w = synth.make_k_grouped(ks, m, n, seed=m + 7, device=dev, ue8m0=True)
+    _assert_pow2(w.sfa, w.sfb)
+    d = w.new_output()
+    c0 = d.clone()
+    dg.k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.ks, c=d, ue8m0=True)
+    torch.cuda.synchronize()
+    _check_k_grouped(w, d, c0, f"k_grouped ue8m0 {ks}")
 
 
 def test_k_grouped_many_groups(dev):

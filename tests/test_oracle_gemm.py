@@ -372,6 +372,11 @@ def pin_ue8m0_power_of_two_identity(orc):
     d0m = np.full((2, 128, 128), 0xFFFF, np.uint16)
     assert np.array_equal(orc.m_grouped_fp8_gemm_nt_masked_ue8m0(am, sfam, b, sfb, counts, d0m),
                           orc.m_grouped_fp8_gemm_nt_masked(am, sfam, b, sfb, counts, d0m))
+    kb_sfb = np.ldexp(1.0, rng.integers(-8, 3, size=(2, 128))).astype(np.float32)
+    ks = [128, 128]
+    np.testing.assert_array_equal(
+        orc.k_grouped_fp8_gemm_nt_contiguous_ue8m0(a[:, :256], sfa[:2], b[0], kb_sfb, ks),
+        orc.k_grouped_fp8_gemm_nt_contiguous(a[:, :256], sfa[:2], b[0], kb_sfb, ks))
 
 
 def pin_ue8m0_drops_mantissa(orc):
