@@ -2,6 +2,13 @@
  * dg.h - FP8 NT GEMM with fine-grained scaling factors and its M-grouped
  * (MoE) variants, for AMD Instinct MI355X (gfx950).
  *
+ * Calls: the dense GEMM and the contiguous, masked and no-padding M-grouped
+ * GEMMs (float32 scales, promoted per 128-K block), the same four with
+ * power-of-two scales applied by the matrix cores (*_ue8m0), the FP8 x FP4
+ * (W4A8) M-grouped GEMMs, and the K-grouped weight-gradient GEMM (float32
+ * output, also *_ue8m0). The general contract below holds for all of them;
+ * each declaration states what differs.
+ *
  * The operation (see the "DeepGEMM for PPU" README, "Interfaces > Notices",
  * "Normal dense GEMMs", "Grouped GEMMs (contiguous layout)" and "Grouped GEMMs
  * (masked layout)"; scale recipe (1, 128, 128) from the "DeepGEMM

@@ -1,7 +1,8 @@
-// Device code shared by the two K-loop pipelines of the FP8 NT GEMM
-// (dg_kernel.hip, dg_kernel_deep.hip): vector types, the LDS swizzle, waits
-// and barriers, buffer descriptors, the tile scheduler of the three layouts
-// and the contiguous layout's row masks.
+// Device code shared by the GEMM kernels (the two FP8 K-loop pipelines
+// dg_kernel.hip and dg_kernel_deep.hip, the K-grouped kernel and the FP8 x FP4
+// kernel): vector types, the LDS swizzle, waits and barriers, buffer
+// descriptors, E8M0 scale codes, the tile scheduler of the M-grouped layouts
+// with its on-device group table, and the contiguous layout's row masks.
 #pragma once
 
 #include <hip/hip_runtime.h>
