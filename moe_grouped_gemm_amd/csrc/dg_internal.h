@@ -64,6 +64,20 @@ struct KGroupedArgs {
 
 hipError_t launch_k_grouped(KGroupedArgs& args, int num_cus, hipStream_t stream);
 
+// Persistent grid size for `tiles` tiles on `slots` resident workgroups: the
+// fewest workgroups that need no more rounds of tiles than `slots` would,
+// above 8 rounded up to a multiple of 8 (so that the kernels' XCD
+// renumbering applies) and capped at `slots`. Fewer workgroups with the same number of
+// rounds measured faster on MI355X (448 tiles: 224 workgroups beat 256 by
+// 3-6%): less contention and power draw, same critical path.
+inline int balanced_grid(long long tiles, long long slots) {
+  if (tiles <= 0 || slots <= 0) return 0;
+  const long long rounds = (tiles + slots - 1) / slots;
+  long long g = (tiles + rounds - 1) / rounds;
+  if (g > 8) g = (g + 7) / 8 * 8;
+  return (int)(g < slots ? g : slots);
+}
+
 // Enqueues the kernel for `kind` on `stream`; arguments already validated.
 hipError_t launch_gemm(int kind, GemmArgs args, int num_cus, hipStream_t stream);
 

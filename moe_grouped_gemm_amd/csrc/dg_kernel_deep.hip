@@ -683,12 +683,8 @@ static hipError_t launch(const GemmArgs& args, int num_cus, hipStream_t stream) 
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, C::THREADS, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
-  const long long slots = (long long)num_cus * per_cu;
-  const long long tiles = args.num_tiles;
-  int grid = (int)(tiles < slots ? tiles : slots);
+  const int grid = balanced_grid(args.num_tiles, (long long)num_cus * per_cu);
   if (grid < 1) return hipSuccess;
-  // Keep a large grid a multiple of 8 so that the XCD renumbering applies.
-  if (grid > 8) grid -= grid & 7;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(C::THREADS), 0, stream, args);
   return hipGetLastError();
 }

@@ -241,10 +241,8 @@ hipError_t launch_fp8_fp4(int kind, GemmArgs args, int num_cus, hipStream_t stre
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, Cfg::THREADS, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
-  const long long slots = (long long)num_cus * per_cu;
-  int grid = (int)(args.num_tiles < slots ? args.num_tiles : slots);
+  const int grid = balanced_grid(args.num_tiles, (long long)num_cus * per_cu);
   if (grid < 1) return hipSuccess;
-  if (grid > 8) grid -= grid & 7;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(Cfg::THREADS), 0, stream, args);
   return hipGetLastError();
 }
