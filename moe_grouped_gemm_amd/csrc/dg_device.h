@@ -245,7 +245,7 @@ __device__ __forceinline__ TileRef resolve_tile(const GemmArgs& p, int t, int nu
     const int per_slot = p.m_blocks * p.n_blocks;
     const int slot = t / per_slot;
     int mb, nb;
-    raster(t - slot * per_slot, p.m_blocks, p.n_blocks, 8, mb, nb);
+    raster(t - slot * per_slot, p.m_blocks, p.n_blocks, 4, mb, nb);
     tr.m0 = mb * C::BM;
     tr.n0 = nb * C::BN;
     tr.load_rows = p.m;
