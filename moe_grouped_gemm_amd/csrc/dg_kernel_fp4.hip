@@ -111,7 +111,9 @@ __device__ __forceinline__ void issue_block(const GemmArgs& p, const Src& s, int
   }
 }
 
-// One K block of a wave's 128 x 64 sub-tile from the stage at `st`.
+// One K block of a wave's 128 x 64 sub-tile from the stage at `st`. The A
+// fragment and scale of band mt + 1 are read before band mt's MFMAs are
+// issued, so that the LDS latency hides behind them.
 __device__ __forceinline__ void block(f32x4 (&acc)[Cfg::MT][Cfg::NT], const uint8_t* st, int wm0, int wn0, int lane) {
   const int r = lane & 15, q = lane >> 4;
   i32x8 bf[Cfg::NT];
@@ -123,17 +125,29 @@ __device__ __forceinline__ void block(f32x4 (&acc)[Cfg::MT][Cfg::NT], const uint
     bf[nt] = (i32x8){x[0], x[1], x[2], x[3], 0, 0, 0, 0};  // an E2M1 operand uses the first four registers
     eb[nt] = e8m0_code(*reinterpret_cast<const float*>(st + SB_OFF + (q * Cfg::BN + row) * 4));
   }
-#pragma unroll
-  for (int mt = 0; mt < Cfg::MT; ++mt) {
+  auto read_a = [&](int mt, i32x8& af, float& sa) {
     const int row = wm0 + mt * 16 + r;
     const i32x4 x = *reinterpret_cast<const i32x4*>(st + lds_offset(row, q));
     const i32x4 y = *reinterpret_cast<const i32x4*>(st + lds_offset(row, q + 4));
-    const i32x8 af = (i32x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-    const int ea = e8m0_code(*reinterpret_cast<const float*>(st + SA_OFF + row * 4));
+    af = (i32x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    sa = *reinterpret_cast<const float*>(st + SA_OFF + row * 4);
+  };
+  i32x8 af[2];
+  float sa[2];
+  read_a(0, af[0], sa[0]);
+#pragma unroll
+  for (int mt = 0; mt < Cfg::MT; ++mt) {
+    if (mt + 1 < Cfg::MT) read_a(mt + 1, af[(mt + 1) & 1], sa[(mt + 1) & 1]);
+    const int ea = e8m0_code(sa[mt & 1]);
 #pragma unroll
     for (int nt = 0; nt < Cfg::NT; ++nt)
       // first operand E2M1 (cbsz 4), second E4M3 (blgp 0)
-      acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af, acc[mt][nt], 4, 0, 0, eb[nt], 0, ea);
+      acc[mt][nt] =
+          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[mt & 1], acc[mt][nt], 4, 0, 0, eb[nt], 0, ea);
+    if (mt + 1 < Cfg::MT) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // the next band's reads first
+    __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);                         // this band's scale code
+    __builtin_amdgcn_sched_group_barrier(0x008, Cfg::NT, 0);                   // then its MFMAs
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

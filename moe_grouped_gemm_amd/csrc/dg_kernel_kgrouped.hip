@@ -129,23 +129,38 @@ __device__ __forceinline__ void block(f32x4 (&acc)[MT][NT], const uint8_t* st, c
     if constexpr (E8) eb[nt] = e8m0_code(*reinterpret_cast<const float*>(st + o.sb_row + nt * 64));
     else sb[nt] = *reinterpret_cast<const f32x4*>(st + o.sb + nt * 64);
   }
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  // The A fragment and scale of band mt + 1 are read before band mt's MFMAs
+  // are issued, so that the LDS latency hides behind them.
+  auto read_a = [&](int mt, i32x8& af, float& sa) {
     const i32x4 x = *reinterpret_cast<const i32x4*>(st + o.a0 + mt * 16 * ROW_BYTES);
     const i32x4 y = *reinterpret_cast<const i32x4*>(st + o.a1 + mt * 16 * ROW_BYTES);
-    const i32x8 af = (i32x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-    const float sa = *reinterpret_cast<const float*>(st + o.sa + mt * 64);
+    af = (i32x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    sa = *reinterpret_cast<const float*>(st + o.sa + mt * 64);
+  };
+  i32x8 af[2];
+  float sa[2];
+  read_a(0, af[0], sa[0]);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    if (mt + 1 < MT) read_a(mt + 1, af[(mt + 1) & 1], sa[(mt + 1) & 1]);
+    const i32x8 a_cur = af[mt & 1];
+    const float s_cur = sa[mt & 1];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       if constexpr (E8) {
-        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af, acc[mt][nt], 0, 0, 0, eb[nt], 0,
-                                                                      e8m0_code(sa));
+        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], a_cur, acc[mt][nt], 0, 0, 0, eb[nt], 0,
+                                                                      e8m0_code(s_cur));
       } else {
-        const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af, (f32x4){0.f, 0.f, 0.f, 0.f},
+        const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], a_cur, (f32x4){0.f, 0.f, 0.f, 0.f},
                                                                            0, 0, 0, 0, 0, 0);
-        acc[mt][nt] += part * (sb[nt] * sa);
+        acc[mt][nt] += part * (sb[nt] * s_cur);
       }
     }
+    if (mt + 1 < MT) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // the next band's reads first
+    if constexpr (E8) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // the scale code
+    __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);                   // this band's MFMAs
+    if constexpr (!E8) __builtin_amdgcn_sched_group_barrier(0x002, 8 * NT, 0);  // its promotion
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
