@@ -151,6 +151,53 @@ __device__ __forceinline__ void block(f32x4 (&acc)[Cfg::MT][Cfg::NT], const uint
   }
 }
 
+// The epilogue's staging area: 16 rows of 128 bytes per wave.
+__device__ __forceinline__ uint8_t* epilogue_buf() {
+  __shared__ __attribute__((aligned(256))) uint8_t buf[Cfg::NW * 16 * ROW_BYTES];
+  return buf;
+}
+
+// Writes a wave's finished 128 x 64 sub-tile as BF16 (round to nearest
+// even), valid rows only. Each 16-row band goes through the wave's own LDS
+// staging area so that every store covers a whole 128-byte row segment (8
+// lanes per row): the band is written in the MFMA layout (lane l holds row
+// l % 16 and 4 columns of each 16-column block), then read back as 8 lanes
+// per row; 16-byte slots are XOR-swizzled by row. Each staging access is a
+// vector load or store at one offset from the staging area's own address.
+template <int KIND>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& cur, const RowMask& cm,
+                                           const f32x4 (&acc)[Cfg::MT][Cfg::NT], int wave, int wm0, int wn0,
+                                           int lane) {
+  static_assert(Cfg::WN * 2 == ROW_BYTES, "one 128-byte row segment per wave and row");
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  uint8_t* const scr = epilogue_buf();
+  const int wbase = wave * 16 * ROW_BYTES;
+  const int r = lane & 15, q = lane >> 4;
+  auto slot_off = [](int row, int sl) { return row * ROW_BYTES + ((sl ^ (row & 7)) << 4); };
+#pragma unroll
+  for (int mt = 0; mt < Cfg::MT; ++mt) {
+    const uint32_t valid = band_rows<Cfg, KIND>(cur, cm, wm0, mt);
+    if (valid == 0) continue;
+#pragma unroll
+    for (int nt = 0; nt < Cfg::NT; ++nt) {
+      const f32x4 v = acc[mt][nt];
+      const i32x2 packed = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
+      // columns 16 nt + 4 q .. + 3: half (q & 1) of 16-byte slot 2 nt + q / 2
+      *reinterpret_cast<i32x2*>(scr + (wbase + slot_off(r, 2 * nt + (q >> 1)) + (q & 1) * 8)) = packed;
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = (lane >> 3) + 8 * half;
+      const int sl = lane & 7;
+      const i32x4 v = *reinterpret_cast<const i32x4*>(scr + (wbase + slot_off(row, sl)));
+      if ((valid >> row) & 1) {
+        uint16_t* drow = cur.d + (size_t)(cur.m0 + wm0 + mt * 16 + row) * p.n + cur.n0 + wn0 + 8 * sl;
+        __builtin_nontemporal_store(v, (global_i32x4*)drow);
+      }
+    }
+  }
+}
+
 template <int KIND>
 __global__ void __launch_bounds__(Cfg::THREADS, 1) fp8_fp4_gemm_kernel(GemmArgs p) {
   const int tid = threadIdx.x;
@@ -216,20 +263,7 @@ __global__ void __launch_bounds__(Cfg::THREADS, 1) fp8_fp4_gemm_kernel(GemmArgs 
     }
     stage = (stage + k_blocks) & 1;
 
-    if (on) {
-#pragma unroll
-      for (int mt = 0; mt < Cfg::MT; ++mt) {
-        const uint32_t valid = band_rows<Cfg, KIND>(cur, cm, wm0, mt);
-        if (!((valid >> r) & 1)) continue;
-        uint16_t* drow = cur.d + (size_t)(cur.m0 + wm0 + mt * 16 + r) * p.n + cur.n0 + wn0 + 4 * q;
-#pragma unroll
-        for (int nt = 0; nt < Cfg::NT; ++nt) {
-          const f32x4 v = acc[mt][nt];
-          const uint2 packed = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          *reinterpret_cast<uint2*>(drow + nt * 16) = packed;
-        }
-      }
-    }
+    if (on) store_tile<KIND>(p, cur, cm, acc, wave, wm0, wn0, lane);
     cur = nxt;
     src = nsrc;
     t = tn;
