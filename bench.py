@@ -30,10 +30,14 @@ METRIC = "TFLOPS & % FP8 MFMA peak: dense, m-grouped contiguous, masked FP8 NT G
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 HEADLINE = 1                 # dense 4096x7168x2048
-# The device code of the kernels (the traffic figures are valid for it only).
-KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_gemm_amd", "csrc", f)
-                  for f in ("dg_device.h", "dg_kernel.hip", "dg_kernel_deep.hip", "dg_kernel_kgrouped.hip",
-                            "dg_kernel_fp4.hip")]
+CSRC = os.path.join(ROOT, "moe_grouped_gemm_amd", "csrc")
+# The device code and launch set-up behind each kernel; a traffic figure is
+# valid only for the code it was counted on.
+KERNEL_SOURCES = {
+    "fp8_gemm_nt_kernel": ("dg_internal.h", "dg_device.h", "dg_kernel.hip", "dg_kernel_deep.hip"),
+    "k_grouped_kernel": ("dg_internal.h", "dg_device.h", "dg_kernel_kgrouped.hip"),
+    "fp8_fp4_gemm_kernel": ("dg_internal.h", "dg_device.h", "dg_kernel_fp4.hip"),
+}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -51,18 +55,25 @@ def parse_args():
     return p.parse_args()
 
 
-def kernel_source_sha() -> str:
+def kernel_of(spec) -> str:
+    """Name of the kernel that runs a workload."""
+    if spec.kind == "k_grouped":
+        return "k_grouped_kernel"
+    return "fp8_fp4_gemm_kernel" if spec.extra.get("fp4") else "fp8_gemm_nt_kernel"
+
+
+def kernel_source_sha(kernel: str) -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload_name: str):
+def read_traffic(spec):
     """HBM bytes per launch from the committed counter summary of this
-    workload, or None if there is none or the kernel source changed since."""
-    path = os.path.join(PROFILES, f"traffic_{workload_name}.txt")
+    workload, or None if there is none or its kernel's source changed since."""
+    path = os.path.join(PROFILES, f"traffic_{spec.name}.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -71,7 +82,7 @@ def read_traffic(workload_name: str):
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 fields[key.strip()] = val.strip()
-    if fields.get("kernel_source_sha256_16") != kernel_source_sha():
+    if fields.get("kernel_source_sha256_16") != kernel_source_sha(kernel_of(spec)):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -174,7 +185,7 @@ def main():
     flops = w.flops()
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
-    traffic = read_traffic(spec.name)
+    traffic = read_traffic(spec)
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -193,8 +204,7 @@ def main():
                    "accumulate": "fp32 with per-128-K promotion", "output": "bf16", "seed": 0},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "kernel": ("k_grouped_kernel" if spec.kind == "k_grouped" else
-                                "fp8_fp4_gemm_kernel" if spec.extra.get("fp4") else "fp8_gemm_nt_kernel"),
+                     "kernel": kernel_of(spec),
                      "kernel_ms": round(kernel_ms, 5),
                      "algorithmic_bytes": w.algorithmic_bytes()},
     }
