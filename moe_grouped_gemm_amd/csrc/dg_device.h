@@ -51,8 +51,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_vmcnt_0() { wait_vmcnt<0>(); }
 
 // Workgroup barrier without the memory fence that __syncthreads() adds: the
-// callers wait on exactly the counters they need first.
-__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
+// callers wait on exactly the counters they need first. The empty asm
+// statements keep the compiler from moving LDS accesses across it: the
+// direct-to-LDS loads write through bare addresses, so to the compiler the
+// stage buffers look unchanged by other waves, and the barrier intrinsic
+// itself touches no memory.
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 __device__ __forceinline__ void wait_lgkmcnt_0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
 
 template <int I, int N, class F>
