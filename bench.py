@@ -9,7 +9,11 @@ JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only INDEX]
                     [--no-cpu-baseline] [--no-extra] [--copy-calibration]
 
---only INDEX times a single workload (0..9), for profiling runs.
+--only INDEX times a single workload (0..12), for profiling runs.
+Besides the back-to-back timing, every workload is also timed cold: before
+each of --cold-iters calls a 1 GiB scratch buffer is read, which evicts the
+L2 caches and the 256 MB Infinity Cache, and each call is timed on its own
+with HIP events (median and minimum reported under "cold").
 --copy-calibration runs a plain 1 GiB device copy (for scaling HBM traffic
 counters) and exits.
 """
@@ -52,6 +56,7 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true")
     p.add_argument("--copy-calibration", action="store_true")
+    p.add_argument("--cold-iters", type=int, default=30)
     return p.parse_args()
 
 
@@ -109,6 +114,43 @@ def time_workload(w, steps: int, warmup: int):
     wall = time.perf_counter() - t0
     kernel_ms = start.elapsed_time(end) / steps
     return wall * 1e3 / steps, kernel_ms
+
+
+FLUSH_BYTES = 1 << 30  # beyond every cache on the path (L2 4 MB per XCD, Infinity Cache 256 MB)
+
+
+def time_cold(w, iters: int, flush):
+    """Per-call kernel times with the caches flushed before each call: the
+    inputs are in HBM only. Returns (median_ms, min_ms)."""
+    import statistics
+    import torch
+    from moe_grouped_gemm_amd import dg
+
+    d = w.new_output()
+    for _ in range(3):
+        dg.run_workload(w, d)
+    stream = torch.cuda.current_stream()
+    events = []
+    for _ in range(iters):
+        flush.view(torch.int64).sum()  # reads 1 GiB: every cache now holds other (clean) lines
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        dg.run_workload(w, d)
+        end.record(stream)
+        events.append((start, end))
+    torch.cuda.synchronize()
+    times = [s.elapsed_time(e) for s, e in events]
+    return statistics.median(times), min(times)
+
+
+def inputs_sha256(w) -> str:
+    """SHA-256 (first 16 hex digits) of a workload's quantised operand and
+    scale bytes, so that runs on different machines can be matched."""
+    from moe_grouped_gemm_amd import synth
+    h = hashlib.sha256()
+    for t in (w.a, w.sfa, w.b, w.sfb):
+        h.update(synth.to_numpy_bytes(t).tobytes())
+    return h.hexdigest()[:16]
 
 
 def cpu_baseline(w, budget_s: float = 20.0):
@@ -182,6 +224,15 @@ def main():
     w = synth.make_workload(spec, seed=0, device=dev)
     torch.cuda.synchronize()
     ms_step, kernel_ms = time_workload(w, args.steps, args.warmup)
+    flush = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device=dev) if args.cold_iters > 0 else None
+
+    def cold_entry(wx):
+        if flush is None:
+            return None
+        med, mn = time_cold(wx, args.cold_iters, flush)
+        return {"median_ms": round(med, 5), "min_ms": round(mn, 5), "iters": args.cold_iters,
+                "tflops_median": round(wx.flops() / (med * 1e-3) / 1e12, 2),
+                "algorithmic_gbs_median": round(wx.algorithmic_bytes() / (med * 1e-3) / 1e9, 1)}
     flops = w.flops()
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
@@ -199,6 +250,8 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8_e4m3",
         "data": "synthetic",
+        "inputs_sha256_16": inputs_sha256(w),
+        "torch": torch.__version__,
         "config": {"workload": spec.name, "kind": spec.kind, "n": spec.n, "k": spec.k,
                    **({"m": spec.m} if spec.kind in ("dense", "k_grouped") else {}),
                    "accumulate": "fp32 with per-128-K promotion", "output": "bf16", "seed": 0},
@@ -212,6 +265,7 @@ def main():
         gbs = w.algorithmic_bytes() / (kernel_ms * 1e-3) / 1e9
         out["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    out["cold"] = cold_entry(w)
 
     if args.only is None and not args.no_extra:
         extra = {}
@@ -227,7 +281,8 @@ def main():
             extra[s.name] = {"kernel_ms": round(kms, 5), "tflops": round(tf, 2),
                              "fp8_peak_frac": round(tf / FP8_PEAK_TFLOPS, 4),
                              "algorithmic_gbs": round(gbs, 1), "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
-                             "valid_rows": getattr(wx, "valid_rows", lambda: s.m)()}
+                             "valid_rows": getattr(wx, "valid_rows", lambda: s.m)(),
+                             "cold": cold_entry(wx)}
             del wx
             torch.cuda.empty_cache()
         out["workloads"] = extra
