@@ -201,8 +201,15 @@ __device__ __forceinline__ StageSrc refill_src(const TileSrc& t0, const TileSrc&
 template <class C>
 struct WaveTile {
   f32x4 acc[C::MT][C::NT];
-  bool on;  // the wave has a valid row and valid columns: it runs its MFMAs and stores
+  bool on;    // the wave has a valid row and valid columns: it runs its MFMAs and stores
+  int bands;  // masked and no-padding layouts: 16-row bands up to the wave's last valid row
 };
+
+// A wave whose valid rows lie in its first HALF_BANDS bands runs a copy of
+// the K loop without the other bands' MFMAs (their rows are never stored).
+// In a masked decode batch most 256-row tiles are partly filled; on such a
+// workload this cut the kernel time by 10% (float32 scales).
+constexpr int HALF_BANDS = 4;
 
 // This lane's LDS byte offsets within a stage, fixed for the kernel. Row
 // `base + (lane & 15)` of a 16-row band with base a multiple of 16 has swizzle
@@ -314,12 +321,15 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& cur
 //              the next step's first A fragments; parts 0 and 1 of the
 //              refill of stage s (step g + 2) are issued.
 // The MFMAs issued before the barrier keep the matrix core busy while the
-// waves meet, and every step starts with its operands in registers.
-template <class C, int KIND, int PHASE, bool E8>
+// waves meet, and every step starts with its operands in registers. Only
+// bands below NB are computed (NB < 8: neither their A fragments are read
+// nor their MFMAs issued); the loads and barriers are the same for every NB.
+template <class C, int KIND, int PHASE, bool E8, int NB>
 __device__ __forceinline__ void mainloop(const GemmArgs& p, const TileSrc& t0, const TileSrc& t1, const TileSrc& t2,
                                          WaveTile<C>& wt, float (&sbv)[2], int wave, const LdsOffsets& lds,
                                          const LaneOffsets& lo, const RowGroups& nrg, int ngroup, RowMask& nmask) {
   static_assert(C::STAGES == 2 && C::MT == 8 && C::NT == 4, "pipeline shape");
+  static_assert(NB == C::MT || (NB >= 2 && NB <= 6), "a partial copy computes bands 0 .. NB-1 before the barrier");
   // The next tile's row mask (contiguous layout), after a barrier: see RowGroups.
   auto next_rows = [&]() {
     if constexpr (KIND == KIND_CONTIGUOUS) {
@@ -366,10 +376,16 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const TileSrc& t0, c
 
 #pragma unroll
       for (int mt = 0; mt < 6; ++mt) {
-        af[(mt + 2) % 4] = frag_at<C, s>(lds.a0, lds.a1, mt + 2);
-        sav[(mt + 2) % 4] = sa_at<C, s>(lds.sa, mt + 2);
+        if (mt + 2 < NB) {
+          af[(mt + 2) % 4] = frag_at<C, s>(lds.a0, lds.a1, mt + 2);
+          sav[(mt + 2) % 4] = sa_at<C, s>(lds.sa, mt + 2);
+        }
         if (mt == 0) issue_part<C, sn, 2>(r1, wave, lo);
         if (mt == 1) sbv[sn] = issue_part<C, sn, 3>(r1, wave, lo);
+        if (mt >= NB) {  // folded at compile time (the loop is unrolled)
+          __builtin_amdgcn_sched_barrier(0);
+          continue;
+        }
         if constexpr (E8) {
           // Power-of-two scales: the MFMA applies them and accumulates.
           const int ea = e8m0_code(sav[mt % 4]);
@@ -404,16 +420,18 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const TileSrc& t0, c
 #pragma unroll
       for (int nt = 0; nt < C::NT; ++nt) {
         f32x4 p6, p7;
-        if constexpr (E8) {
-          wt.acc[6][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[6 % 4], wt.acc[6][nt],
-                                                                          0, 0, 0, eb, 0, ea6);
-          wt.acc[7][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[7 % 4], wt.acc[7][nt],
-                                                                          0, 0, 0, eb, 0, ea7);
-        } else {
-          p6 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[6 % 4], (f32x4){0.f, 0.f, 0.f, 0.f},
-                                                               0, 0, 0, 0, 0, 0);
-          p7 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[7 % 4], (f32x4){0.f, 0.f, 0.f, 0.f},
-                                                               0, 0, 0, 0, 0, 0);
+        if constexpr (NB == C::MT) {
+          if constexpr (E8) {
+            wt.acc[6][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[6 % 4], wt.acc[6][nt],
+                                                                            0, 0, 0, eb, 0, ea6);
+            wt.acc[7][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[7 % 4], wt.acc[7][nt],
+                                                                            0, 0, 0, eb, 0, ea7);
+          } else {
+            p6 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[6 % 4], (f32x4){0.f, 0.f, 0.f, 0.f},
+                                                                 0, 0, 0, 0, 0, 0);
+            p7 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[7 % 4], (f32x4){0.f, 0.f, 0.f, 0.f},
+                                                                 0, 0, 0, 0, 0, 0);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         if (nt == 0) {
@@ -436,7 +454,7 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const TileSrc& t0, c
           af[1] = frag_at<C, sn>(lds.a0, lds.a1, 1);
           sav[1] = sa_at<C, sn>(lds.sa, 1);
         }
-        if constexpr (!E8) {
+        if constexpr (!E8 && NB == C::MT) {
           wt.acc[6][nt] += p6 * w6;
           wt.acc[7][nt] += p7 * w7;
         }
@@ -522,6 +540,9 @@ __global__ void __launch_bounds__(C::THREADS, 1) fp8_gemm_nt_kernel(GemmArgs p) 
     if constexpr (KIND == KIND_CONTIGUOUS) any_row = (cmask.even | cmask.odd) != 0;
     else any_row = cur.valid_rows > cur.m0 + wm0;
     wt.on = any_row && (cur.n0 + wn0 < p.n);
+    wt.bands = C::MT;
+    if constexpr (counts_on_device(KIND))
+      wt.bands = uniform_int(min(max((cur.valid_rows - cur.m0 - wm0 + 15) / 16, 0), C::MT));
     RowGroups nrg{-1, -1};
     if constexpr (KIND == KIND_CONTIGUOUS) nrg = load_row_groups<C>(p, nxt, wm0, lane);
 #pragma unroll
@@ -529,8 +550,13 @@ __global__ void __launch_bounds__(C::THREADS, 1) fp8_gemm_nt_kernel(GemmArgs p) 
 #pragma unroll
       for (int nt = 0; nt < C::NT; ++nt) wt.acc[mt][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    if (phase == 0) mainloop<C, KIND, 0, E8>(p, c0, c1, c2, wt, sbv, wave, lds, lo, nrg, nxt.group, nmask);
-    else mainloop<C, KIND, 1, E8>(p, c0, c1, c2, wt, sbv, wave, lds, lo, nrg, nxt.group, nmask);
+    if (counts_on_device(KIND) && wt.bands <= HALF_BANDS) {
+      if (phase == 0) mainloop<C, KIND, 0, E8, HALF_BANDS>(p, c0, c1, c2, wt, sbv, wave, lds, lo, nrg, nxt.group, nmask);
+      else mainloop<C, KIND, 1, E8, HALF_BANDS>(p, c0, c1, c2, wt, sbv, wave, lds, lo, nrg, nxt.group, nmask);
+    } else {
+      if (phase == 0) mainloop<C, KIND, 0, E8, C::MT>(p, c0, c1, c2, wt, sbv, wave, lds, lo, nrg, nxt.group, nmask);
+      else mainloop<C, KIND, 1, E8, C::MT>(p, c0, c1, c2, wt, sbv, wave, lds, lo, nrg, nxt.group, nmask);
+    }
     phase = (phase + k_blocks) % C::STAGES;
 
     // Epilogue (the next tile's first K block has landed, its second is in
