@@ -267,6 +267,31 @@ def test_masked_many_groups(dev):
     _check_masked(w, d, counts, "masked many groups")
 
 
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_masked_partial_band_copies(dev, ue8m0):
+    """Valid rows ending at and next to the 64-row boundary of each wave's
+    128 rows (below it the wave runs the K loop copy without bands 4-7).
+    Three workgroups take all 24 tiles, so copies alternate within one
+    workgroup; 5 K blocks make consecutive tiles start on alternating
+    stages."""
+    counts = [64, 65, 192, 193, 48, 80, 16, 17, 256, 0, 1, 129]
+    _say(f"masked partial bands ue8m0={ue8m0}")
+    w = synth.make_masked(counts, 256, 512, 640, seed=7, device=dev, poison_invalid=True, ue8m0=ue8m0)
+    d = w.new_output()
+    dg.set_num_cus(3)
+    try:
+        dg.m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m, ue8m0=ue8m0)
+        torch.cuda.synchronize()
+    finally:
+        dg.set_num_cus(0)
+    _check_masked(w, d, counts, "masked partial bands")
+    d_full = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d_full, w.masked_m, ue8m0=ue8m0)
+    torch.cuda.synchronize()
+    # the grid size changes which tiles share a workgroup, not the arithmetic
+    assert torch.equal(d.view(torch.int16), d_full.view(torch.int16))
+
+
 # ---------------------------------------------------------------------------
 # No-padding layout
 # ---------------------------------------------------------------------------
