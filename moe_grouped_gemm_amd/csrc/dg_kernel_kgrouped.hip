@@ -236,16 +236,35 @@ __global__ void __launch_bounds__(THREADS, 1) k_grouped_kernel(KGroupedArgs p) {
     loaded = next_loaded;
 
     if (on) {
+      // Two bands at a time: all their C loads first, then the sums and the
+      // stores. C and D may be one buffer, so the compiler keeps every load
+      // after the stores before it; loading and storing element by element
+      // made each load wait for the one before (32 round trips per tile,
+      // a quarter of the kernel time). Each element is read and written by
+      // this lane only, so reading ahead of the stores is safe.
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = tl.m0 + wm0 + mt * 16 + r;
-        if (m >= p.m) continue;
+      for (int m2 = 0; m2 < MT; m2 += 2) {
+        f32x4 cv[2][NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const size_t idx = ((size_t)tl.g * p.m + m) * p.n + tl.n0 + wn0 + nt * 16 + 4 * q;
-          f32x4 v = acc[mt][nt];
-          if constexpr (HAS_C) v += *reinterpret_cast<const f32x4*>(p.c + idx);
-          *reinterpret_cast<f32x4*>(p.d + idx) = v;
+        for (int h = 0; h < 2; ++h) {
+          const int m = tl.m0 + wm0 + (m2 + h) * 16 + r;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            cv[h][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            if (HAS_C && m < p.m)
+              cv[h][nt] = *reinterpret_cast<const f32x4*>(p.c + ((size_t)tl.g * p.m + m) * p.n + tl.n0 + wn0 +
+                                                          nt * 16 + 4 * q);
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int m = tl.m0 + wm0 + (m2 + h) * 16 + r;
+          if (m >= p.m) continue;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const size_t idx = ((size_t)tl.g * p.m + m) * p.n + tl.n0 + wn0 + nt * 16 + 4 * q;
+            *reinterpret_cast<f32x4*>(p.d + idx) = acc[m2 + h][nt] + cv[h][nt];
+          }
         }
       }
     }
