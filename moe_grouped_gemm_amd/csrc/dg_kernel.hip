@@ -298,9 +298,11 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileRef& cur
       const i32x4 q = *reinterpret_cast<const i32x4*>(st + (wbase + slot_off(row, sl)));
       if ((valid >> row) & 1) {
         uint16_t* drow = cur.d + (size_t)(cur.m0 + wm0 + mt * 16 + row) * p.n + cur.n0 + wn0 + 8 * sl;
-        // A global (not flat) store, which the LDS counter does not track, and
-        // non-temporal: the output is not read again by this kernel.
-        __builtin_nontemporal_store(q, (global_i32x4*)drow);
+        // A global (not flat) store, which the LDS counter does not track.
+        // Non-temporal for the grouped layouts (plain stores made masked decode
+        // 10% slower); plain for the dense GEMM, 2-3% faster there.
+        if constexpr (KIND == KIND_DENSE) *(global_i32x4*)drow = q;
+        else __builtin_nontemporal_store(q, (global_i32x4*)drow);
       }
     }
   }
