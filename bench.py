@@ -143,6 +143,27 @@ def time_cold(w, iters: int, flush):
     return statistics.median(times), min(times)
 
 
+def copy_ceiling_gbs(buf) -> float:
+    """Bytes moved (read + written) per second by a device-to-device copy of
+    a 1 GiB buffer: the HBM rate a plain streaming kernel reaches here."""
+    import statistics
+    import torch
+    dst = torch.empty_like(buf)
+    for _ in range(3):
+        dst.copy_(buf)
+    times = []
+    for _ in range(10):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        dst.copy_(buf)
+        e.record()
+        times.append((s, e))
+    torch.cuda.synchronize()
+    ms = statistics.median([a.elapsed_time(b) for a, b in times])
+    del dst
+    return 2 * buf.numel() * buf.element_size() / (ms * 1e-3) / 1e9
+
+
 def inputs_sha256(w) -> str:
     """SHA-256 (first 16 hex digits) of a workload's quantised operand and
     scale bytes, so that runs on different machines can be matched."""
@@ -252,6 +273,7 @@ def main():
         "data": "synthetic",
         "inputs_sha256_16": inputs_sha256(w),
         "torch": torch.__version__,
+        "numpy": __import__("numpy").__version__,
         "config": {"workload": spec.name, "kind": spec.kind, "n": spec.n, "k": spec.k,
                    **({"m": spec.m} if spec.kind in ("dense", "k_grouped") else {}),
                    "accumulate": "fp32 with per-128-K promotion", "output": "bf16", "seed": 0},
@@ -266,6 +288,8 @@ def main():
         out["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(gbs / HBM_PEAK_GBS, 4)})
     out["cold"] = cold_entry(w)
+    if flush is not None:
+        out["hbm_copy_gbs"] = round(copy_ceiling_gbs(flush), 1)
 
     if args.only is None and not args.no_extra:
         extra = {}
