@@ -524,6 +524,30 @@ def test_fp8_fp4_masked_small(dev, counts, max_m, n, k):
         check_untouched(got[g, v:], f"w4a8 masked group {g} rows >= {v}")
 
 
+def test_fp8_fp4_masked_partial_band_copies(dev):
+    """Valid rows ending at and next to the 64-row boundary of each wave's 128
+    rows (below it the wave runs the K loop copy without bands 4-7), with
+    three workgroups taking all tiles so that both copies alternate in one
+    workgroup."""
+    counts = [64, 65, 192, 193, 48, 80, 16, 17, 256, 0, 1, 129]
+    _say("w4a8 masked partial bands")
+    w = synth.make_masked(counts, 256, 512, 640, seed=37, device=dev, poison_invalid=True, fp4=True)
+    d = w.new_output()
+    dg.set_num_cus(3)
+    try:
+        dg.m_grouped_fp8_fp4_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m)
+        torch.cuda.synchronize()
+    finally:
+        dg.set_num_cus(0)
+    got = NP(d)
+    for g, c in enumerate(counts):
+        v = min(max(int(c), 0), 256)
+        if v:
+            check_close(got[g, :v], _fp4_ref_rows(w, g, np.arange(v), np.arange(512), NP(w.a)[g], NP(w.sfa)[g]),
+                        f"w4a8 masked partial bands group {g}")
+        check_untouched(got[g, v:], f"w4a8 masked partial bands group {g} rows >= {v}")
+
+
 def test_fp8_fp4_integer_exact_bitwise(dev):
     """A codes in {-2..2}, B any E2M1 value, scales 2^-1..2^1: every product
     and partial sum is exact in float32, so the output matches bit for bit."""
