@@ -45,8 +45,14 @@ design notes of the repository):
   * FP8 flavour: OCP E4M3 (bias 7, max 448, codes 0x7F/0xFF are NaN, no inf).
   * BF16 rounding: round to nearest, ties to even, applied once to the exact
     float64 sum (no intermediate rounding to float32).
-  * contiguous layout: row m belongs to group L[m] when 0 <= L[m] < G; any
-    other id (-1 marks padding) leaves row m of D untouched.
+  * contiguous layout: the layout is a sequence of 128-row blocks, each
+    holding one group's rows (segments are aligned to the M block). A
+    block belongs to the group named by its first row's id; row m is
+    computed, for group L[m], when L[m] is that id and lies in [0, G). Any
+    other row (id -1 for padding, an id outside [0, G), or an id that
+    differs from its block's) is left untouched. For layouts whose segments
+    really are 128-row aligned this is simply "row m belongs to L[m] when
+    0 <= L[m] < G".
   * masked layout: masked_m[g] is clamped to [0, max_m]; rows at or beyond it
     are left untouched.
   * no-padding layout: the count tensor holds one int32 row count per group;
@@ -85,8 +91,10 @@ __all__ = [
     "dequant_lhs",
     "dequant_rhs",
     "gemm_nt_f64",
+    "gemm_nt_exact",
     "dense_f64_at",
     "fp8_gemm_nt",
+    "contiguous_row_groups",
     "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked",
     "nopad_row_ranges",
@@ -204,20 +212,40 @@ def dequant_lhs(a_codes: np.ndarray, sfa: np.ndarray) -> np.ndarray:
     return values * np.repeat(scale, BLOCK_K, axis=1)
 
 
-def dequant_rhs(b_codes: np.ndarray, sfb: np.ndarray) -> np.ndarray:
+def dequant_rhs(b_codes: np.ndarray, sfb: np.ndarray, rows=None) -> np.ndarray:
     """Bhat[n,k] = dec(B[n,k]) * sfb[n // 128][k // 128].
 
     b_codes: uint8 [N, K] (the transposed RHS of the NT product).
     sfb:     float32 [ceil(N/128), K/128].
+    rows:    None for all N rows, else the row indices n to dequantise (the
+             result then has one row per index, in that order).
     """
     b_codes = np.asarray(b_codes, dtype=np.uint8)
     n, k = b_codes.shape
     assert k % BLOCK_K == 0
     assert sfb.shape == ((n + BLOCK_K - 1) // BLOCK_K, k // BLOCK_K)
-    values = e4m3_decode_table()[b_codes]                       # [N, K]
-    scale = np.asarray(sfb, dtype=np.float64)
-    scale = np.repeat(np.repeat(scale, BLOCK_K, axis=0)[:n], BLOCK_K, axis=1)
-    return values * scale
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    values = e4m3_decode_table()[b_codes[rows]]                 # [len(rows), K]
+    scale = np.asarray(sfb, dtype=np.float64)[rows // BLOCK_K]  # [len(rows), K/128]
+    return values * np.repeat(scale, BLOCK_K, axis=1)
+
+
+def gemm_nt_exact(a_codes, sfa, b_codes, sfb) -> list:
+    """The dense result in exact rational arithmetic, element by element:
+    sum_k dec(A[m,k]) sfa[k // 128][m] dec(B[n,k]) sfb[n // 128][k // 128]
+    as a list of lists of fractions.Fraction (every E4M3 value and float32
+    scale is a dyadic rational, so nothing is rounded). Brute force for tiny
+    shapes only."""
+    from fractions import Fraction
+    a_codes = np.asarray(a_codes, dtype=np.uint8)
+    b_codes = np.asarray(b_codes, dtype=np.uint8)
+    m_rows, k = a_codes.shape
+    n = b_codes.shape[0]
+    dec = [Fraction(e4m3_value(c)) if c & 0x7F != 0x7F else None for c in range(256)]
+    ahat = [[dec[a_codes[i, kk]] * Fraction(float(sfa[kk // BLOCK_K][i])) for kk in range(k)] for i in range(m_rows)]
+    bhat = [[dec[b_codes[j, kk]] * Fraction(float(sfb[j // BLOCK_K][kk // BLOCK_K])) for kk in range(k)]
+            for j in range(n)]
+    return [[sum((x * y for x, y in zip(ahat[i], bhat[j])), Fraction(0)) for j in range(n)] for i in range(m_rows)]
 
 
 def gemm_nt_f64(a_codes, sfa, b_codes, sfb) -> np.ndarray:
@@ -242,20 +270,35 @@ def fp8_gemm_nt(a_codes, sfa, b_codes, sfb, d_init=None) -> np.ndarray:
     return d
 
 
+def contiguous_row_groups(layout, num_groups: int) -> np.ndarray:
+    """Group of each row of the contiguous layout, -1 for rows not computed.
+
+    The rows form blocks of 128 (the M-block alignment of the segments); a
+    block belongs to the group named by the id of its first row. Row m gets
+    group L[m] when L[m] equals its block's id and 0 <= L[m] < G, else -1.
+    M must be a multiple of 128.
+    """
+    layout = np.asarray(layout, dtype=np.int64)
+    assert layout.size % BLOCK_K == 0, "contiguous layouts hold whole 128-row blocks"
+    block_id = np.repeat(layout[::BLOCK_K], BLOCK_K)
+    ok = (layout == block_id) & (layout >= 0) & (layout < num_groups)
+    return np.where(ok, layout, -1)
+
+
 def m_grouped_fp8_gemm_nt_contiguous(a_codes, sfa, b_codes, sfb, layout, d_init) -> np.ndarray:
     """M-grouped GEMM, contiguous layout.
 
     a_codes [M, K], sfa [K/128, ld], b_codes [G, N, K], sfb [G, N/128, K/128],
-    layout int32 [M] (group of each row; -1 or any id outside [0, G) marks a
-    row that is not computed), d_init uint16 [M, N] (prior contents of D).
-    Row m of D becomes bf16(Ahat[m] . Bhat_{L[m]}^T) when 0 <= L[m] < G and is
-    copied from d_init otherwise.
+    layout int32 [M] (group of each row, -1 for padding), d_init uint16
+    [M, N] (prior contents of D). Row m of D becomes
+    bf16(Ahat[m] . Bhat_g^T) for g = contiguous_row_groups(layout, G)[m] >= 0
+    and is copied from d_init otherwise.
     """
-    layout = np.asarray(layout, dtype=np.int64)
     num_groups = b_codes.shape[0]
+    owner = contiguous_row_groups(layout, num_groups)
     d = np.array(d_init, dtype=np.uint16, copy=True)
     for g in range(num_groups):
-        rows = np.nonzero(layout == g)[0]
+        rows = np.nonzero(owner == g)[0]
         if rows.size == 0:
             continue
         ahat = dequant_lhs(a_codes[rows], sfa[:, rows])
@@ -320,62 +363,72 @@ def m_grouped_fp8_gemm_nt_nopad(a_codes, sfa, b_codes, sfb, group_rows, d_init) 
 # Sampled evaluation for full-size checks: a subset of rows and columns.
 # ---------------------------------------------------------------------------
 
-def _rows_cols_f64(a_codes, sfa, b_codes, sfb, rows, cols) -> np.ndarray:
-    """sum_k Ahat[r,k] Bhat[c,k] for r in rows, c in cols (one group)."""
+def _rows_cols_f64(a_codes, sfa, b_codes, sfb, rows, cols, abs_sum=False):
+    """sum_k Ahat[r,k] Bhat[c,k] for r in rows, c in cols (one group), from
+    dequant_lhs and dequant_rhs on those rows; with abs_sum also
+    sum_k |Ahat[r,k] Bhat[c,k]| (for error bounds)."""
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
-    k = a_codes.shape[1]
-    table = e4m3_decode_table()
-    a_val = table[np.asarray(a_codes[rows], dtype=np.uint8)]
-    a_scale = np.asarray(sfa, dtype=np.float64)[:, rows].T
-    ahat = a_val * np.repeat(a_scale, BLOCK_K, axis=1)
-    b_val = table[np.asarray(b_codes[cols], dtype=np.uint8)]
-    b_scale = np.asarray(sfb, dtype=np.float64)[cols // BLOCK_K]
-    bhat = b_val * np.repeat(b_scale, BLOCK_K, axis=1)
-    assert ahat.shape[1] == k and bhat.shape[1] == k
-    return ahat @ bhat.T
+    ahat = dequant_lhs(np.asarray(a_codes)[rows], np.asarray(sfa)[:, rows])
+    bhat = dequant_rhs(b_codes, sfb, cols)
+    val = ahat @ bhat.T
+    return (val, np.abs(ahat) @ np.abs(bhat).T) if abs_sum else val
 
 
-def dense_f64_at(a_codes, sfa, b_codes, sfb, rows, cols) -> np.ndarray:
-    """Unrounded dense result at rows x cols."""
-    return _rows_cols_f64(a_codes, sfa, b_codes, sfb, rows, cols)
+def _nan_like(rows, cols, abs_sum):
+    out = np.full((len(rows), len(cols)), np.nan)
+    return (out, out.copy()) if abs_sum else out
 
 
-def contiguous_f64_at(a_codes, sfa, b_codes, sfb, layout, rows, cols) -> np.ndarray:
+def _put(out, sel, val, abs_sum):
+    if abs_sum:
+        out[0][sel], out[1][sel] = val
+    else:
+        out[sel] = val
+
+
+def dense_f64_at(a_codes, sfa, b_codes, sfb, rows, cols, abs_sum=False):
+    """Unrounded dense result at rows x cols (with abs_sum: (value, sum of
+    the products' magnitudes))."""
+    return _rows_cols_f64(a_codes, sfa, b_codes, sfb, rows, cols, abs_sum)
+
+
+def contiguous_f64_at(a_codes, sfa, b_codes, sfb, layout, rows, cols, abs_sum=False):
     """Unrounded contiguous-layout result at rows x cols; NaN where a row is
-    not computed (its group id is outside [0, G))."""
-    layout = np.asarray(layout, dtype=np.int64)
+    not computed (contiguous_row_groups gives it no group)."""
+    owner = contiguous_row_groups(layout, b_codes.shape[0])
     rows = np.asarray(rows, dtype=np.int64)
-    out = np.full((rows.size, len(cols)), np.nan)
+    out = _nan_like(rows, cols, abs_sum)
     for g in range(b_codes.shape[0]):
-        sel = np.nonzero(layout[rows] == g)[0]
+        sel = np.nonzero(owner[rows] == g)[0]
         if sel.size:
-            out[sel] = _rows_cols_f64(a_codes, sfa, b_codes[g], sfb[g], rows[sel], cols)
+            _put(out, sel, _rows_cols_f64(a_codes, sfa, b_codes[g], sfb[g], rows[sel], cols, abs_sum), abs_sum)
     return out
 
 
-def masked_f64_at(a_codes, sfa, b_codes, sfb, masked_m, group, rows, cols) -> np.ndarray:
+def masked_f64_at(a_codes, sfa, b_codes, sfb, masked_m, group, rows, cols, abs_sum=False):
     """Unrounded masked-layout result of one group at rows x cols; NaN for
     rows at or beyond the group's clamped valid count."""
     max_m = a_codes.shape[1]
     valid = int(min(max(int(masked_m[group]), 0), max_m))
     rows = np.asarray(rows, dtype=np.int64)
-    out = np.full((rows.size, len(cols)), np.nan)
+    out = _nan_like(rows, cols, abs_sum)
     sel = np.nonzero(rows < valid)[0]
     if sel.size:
-        out[sel] = _rows_cols_f64(a_codes[group], sfa[group], b_codes[group], sfb[group], rows[sel], cols)
+        _put(out, sel, _rows_cols_f64(a_codes[group], sfa[group], b_codes[group], sfb[group], rows[sel], cols,
+                                      abs_sum), abs_sum)
     return out
 
 
-def nopad_f64_at(a_codes, sfa, b_codes, sfb, group_rows, rows, cols) -> np.ndarray:
+def nopad_f64_at(a_codes, sfa, b_codes, sfb, group_rows, rows, cols, abs_sum=False):
     """Unrounded no-padding-layout result at rows x cols; NaN for rows that
     no group owns."""
     rows = np.asarray(rows, dtype=np.int64)
-    out = np.full((rows.size, len(cols)), np.nan)
+    out = _nan_like(rows, cols, abs_sum)
     for g, (first, end) in enumerate(nopad_row_ranges(group_rows, a_codes.shape[0])):
         sel = np.nonzero((rows >= first) & (rows < end))[0]
         if sel.size:
-            out[sel] = _rows_cols_f64(a_codes, sfa, b_codes[g], sfb[g], rows[sel], cols)
+            _put(out, sel, _rows_cols_f64(a_codes, sfa, b_codes[g], sfb[g], rows[sel], cols, abs_sum), abs_sum)
     return out
 
 
@@ -459,8 +512,9 @@ def k_grouped_fp8_gemm_nt_contiguous_ue8m0(a_codes, sfa, b_codes, sfb, ks, c_ini
 
 
 def k_grouped_f64_at(a_codes, sfa, b_codes, sfb, ks, group, rows, cols, c_init=None, abs_sum=False):
-    """Group `group`'s result at rows x cols (float64); with abs_sum also
-    sum_k |Ahat[r, k] Bhat[c, k]| + |C| there (for error bounds)."""
+    """Group `group`'s result at rows x cols (float64), from _k_group_operands
+    on those rows of A and B; with abs_sum also sum_k |Ahat[r, k] Bhat[c, k]|
+    + |C| there (for error bounds)."""
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
     k0, k1 = k_grouped_ranges(ks)[group]
@@ -468,8 +522,8 @@ def k_grouped_f64_at(a_codes, sfa, b_codes, sfb, ks, group, rows, cols, c_init=N
     if k1 == k0:
         val, mag = c.copy(), np.abs(c)
     else:
-        ahat = dequant_lhs(a_codes[rows][:, k0:k1], sfa[k0 // BLOCK_K:k1 // BLOCK_K][:, rows])
-        bhat = dequant_lhs(b_codes[cols][:, k0:k1], sfb[k0 // BLOCK_K:k1 // BLOCK_K][:, cols])
+        ahat, bhat = _k_group_operands(np.asarray(a_codes)[rows], np.asarray(sfa)[:, rows],
+                                       np.asarray(b_codes)[cols], np.asarray(sfb)[:, cols], k0, k1)
         val = c + ahat @ bhat.T
         mag = np.abs(c) + np.abs(ahat) @ np.abs(bhat).T
     return (val, mag) if abs_sum else val
@@ -521,11 +575,11 @@ def m_grouped_fp8_fp4_gemm_nt_contiguous(a_codes, sfa, b_packed, sfb, layout, d_
     """Contiguous-layout FP8 x FP4 GEMM: as m_grouped_fp8_gemm_nt_contiguous
     with Bhat_g from dequant_rhs_e2m1 and every scale read as E8M0.
     b_packed [G, N, K/2], sfb [G, K/32, ld >= N]."""
-    layout = np.asarray(layout, dtype=np.int64)
+    owner = contiguous_row_groups(layout, b_packed.shape[0])
     d = np.array(d_init, dtype=np.uint16, copy=True)
     sfa_v = e8m0_value(sfa)
     for g in range(b_packed.shape[0]):
-        rows = np.nonzero(layout == g)[0]
+        rows = np.nonzero(owner == g)[0]
         if rows.size == 0:
             continue
         ahat = dequant_lhs(a_codes[rows], sfa_v[:, rows])
@@ -548,14 +602,15 @@ def m_grouped_fp8_fp4_gemm_nt_masked(a_codes, sfa, b_packed, sfb, masked_m, d_in
     return d
 
 
-def fp8_fp4_f64_at(a_codes, sfa, b_packed_g, sfb_g, rows, cols) -> np.ndarray:
-    """Unrounded FP8 x FP4 result of one group at rows x cols: a_codes [M, K]
-    and sfa [K/128, ld] of that group's rows, b_packed_g [N, K/2],
-    sfb_g [K/32, ld]."""
+def fp8_fp4_f64_at(a_codes, sfa, b_packed_g, sfb_g, rows, cols, abs_sum=False):
+    """Unrounded FP8 x FP4 result of one group at rows x cols, from
+    dequant_lhs (E8M0 LHS scales) and dequant_rhs_e2m1 on those rows:
+    a_codes [M, K] and sfa [K/128, ld] of that group's rows,
+    b_packed_g [N, K/2], sfb_g [K/32, ld]; with abs_sum also the sum of the
+    products' magnitudes."""
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
-    ahat = dequant_lhs(a_codes[rows], e8m0_value(sfa)[:, rows])
-    codes = unpack_e2m1(np.asarray(b_packed_g)[cols])
-    scale = e8m0_value(np.asarray(sfb_g))[:, cols].T
-    bhat = e2m1_decode_table()[codes] * np.repeat(scale, FP4_BLOCK_K, axis=1)
-    return ahat @ bhat.T
+    ahat = dequant_lhs(np.asarray(a_codes)[rows], e8m0_value(np.asarray(sfa)[:, rows]))
+    bhat = dequant_rhs_e2m1(np.asarray(b_packed_g)[cols], np.asarray(sfb_g)[:, cols])
+    val = ahat @ bhat.T
+    return (val, np.abs(ahat) @ np.abs(bhat).T) if abs_sum else val

@@ -146,6 +146,15 @@ def pin_exact_dense(orc):
     _check_against_exact(f64, bits, exact, fa, fb)
 
 
+def pin_exact_brute_force_matches(orc):
+    """The oracle's exact-rational brute force equals this file's, which
+    decodes through torch instead of the OCP formula."""
+    rng = np.random.default_rng(29)
+    a, sfa, b, sfb = _random_inputs(rng, 2, 128, 256)
+    exact, _, _ = _exact_gemm(a, sfa, b, sfb)
+    assert orc.gemm_nt_exact(a, sfa, b, sfb) == exact
+
+
 def pin_exact_grouped(orc):
     rng = np.random.default_rng(11)
     a, sfa, b, sfb = _random_inputs(rng, 256, 128, 256, groups=2)
@@ -588,10 +597,169 @@ def pin_near_tie_gemm(orc):
     assert int(orc.fp8_gemm_nt(a, sfa, b, sfb)[0, 0]) == 0x3F81
 
 
+# ---------------------------------------------------------------------------
+# The contiguous layout's row rule, and the sampled-evaluation functions that
+# the full-size GPU checks use as their reference
+# ---------------------------------------------------------------------------
+
+def _contiguous_owner_walk(layout, num_groups):
+    """Owner of each row, walked block by block: a 128-row block takes the id
+    of its first row; a row is computed for that id when its own id is the
+    same and the id names a group."""
+    owner = []
+    for start in range(0, len(layout), 128):
+        block_id = int(layout[start])
+        for r in range(start, start + 128):
+            ok = int(layout[r]) == block_id and 0 <= block_id < num_groups
+            owner.append(block_id if ok else -1)
+    return np.array(owner)
+
+
+def pin_contiguous_block_rule(orc):
+    """Ids that change inside a 128-row block: only rows whose id is their
+    block's first-row id (and names a group) are written, each equal to a
+    dense GEMM of its group; aligned layouts write every row with a valid id."""
+    rng = np.random.default_rng(83)
+    g_count, n, k = 3, 128, 256
+    layout = np.full(512, -1, np.int32)
+    layout[0:100] = 0          # block 0: group 0, rows 100..127 padding
+    layout[100:128] = 1        # ... and rows of group 1 inside group 0's block (not written)
+    layout[128:200] = 1        # block 1: group 1
+    layout[200:256] = 2        # ... group 2 inside group 1's block (not written)
+    layout[256] = -1           # block 2 starts with padding: nothing in it is written
+    layout[257:300] = 2
+    layout[384:500] = 5        # block 3: an id outside [0, G): nothing written
+    a, sfa, b, sfb = _random_inputs(rng, 512, n, k, groups=g_count)
+    d0 = np.full((512, n), 0xFFFF, np.uint16)
+    d = orc.m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, layout, d0)
+    owner = _contiguous_owner_walk(layout, g_count)
+    assert np.array_equal(orc.contiguous_row_groups(layout, g_count), owner)
+    assert np.array_equal(np.nonzero(owner >= 0)[0], np.r_[0:100, 128:200])
+    assert np.all(d[owner < 0] == 0xFFFF)
+    for g in range(g_count):
+        idx = np.nonzero(owner == g)[0]
+        if idx.size:
+            sub_sfa = np.pad(sfa[:, idx], ((0, 0), (0, (-idx.size) % 4)))
+            assert np.array_equal(d[idx], orc.fp8_gemm_nt(a[idx], sub_sfa, b[g], sfb[g]))
+    aligned = np.r_[np.zeros(100), np.full(28, -1), np.full(128, 2), np.ones(60), np.full(68, -1)].astype(np.int32)
+    assert np.array_equal(orc.contiguous_row_groups(aligned, g_count), np.where(aligned >= 0, aligned, -1))
+    fp4 = orc.m_grouped_fp8_fp4_gemm_nt_contiguous(
+        a, np.ldexp(1.0, np.round(np.log2(sfa)).astype(np.int64)).astype(np.float32),
+        rng.integers(0, 256, size=(g_count, n, k // 2)).astype(np.uint8),
+        np.ones((g_count, k // 32, n), np.float32), layout, d0)
+    assert np.all(fp4[owner < 0] == 0xFFFF) and np.all(fp4[owner >= 0] != 0xFFFF)
+
+
+def _int_codes(rng, shape):
+    return np.vectorize(CODE_OF.get)(rng.integers(-2, 3, size=shape)).astype(np.uint8)
+
+
+def _pow2(rng, shape, lo=-2, hi=3):
+    return np.ldexp(1.0, rng.integers(lo, hi, size=shape)).astype(np.float32)
+
+
+def _abs_codes(c):
+    return (np.asarray(c, np.uint8) & 0x7F).astype(np.uint8)
+
+
+def pin_sampled_functions_match_full(orc):
+    """Each *_f64_at function equals its full oracle counterpart on the rows
+    and columns it is asked for (first and last rows of every group included),
+    and is NaN exactly where the full function leaves D untouched; with
+    abs_sum its magnitude equals the full function run on |operands|.
+    Integer-valued codes and power-of-two scales make every sum exact, so the
+    comparisons are exact."""
+    rng = np.random.default_rng(89)
+    n, k = 256, 384
+    sentinel = 0xFFFF
+
+    def bits_or_nan(vals):
+        out = orc.bf16_bits(np.nan_to_num(vals))
+        out[np.isnan(vals)] = sentinel
+        return out
+
+    # contiguous: three aligned segments with padding, one empty group
+    rows_g = [130, 0, 77, 128]
+    layout = np.concatenate([np.r_[np.full(r, g), np.full((-r) % 128, -1)] for g, r in enumerate(rows_g)])
+    layout = layout.astype(np.int32)
+    m = layout.size
+    a, b = _int_codes(rng, (m, k)), _int_codes(rng, (4, n, k))
+    sfa, sfb = _pow2(rng, (k // 128, m)), _pow2(rng, (4, n // 128, k // 128))
+    full = orc.m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, layout, np.full((m, n), sentinel, np.uint16))
+    rows = np.r_[0, 1, 129, 130, 255, 256, 332, 333, 383, 384, 511]
+    cols = np.r_[0, 5, 127, 128, 255]
+    val, mag = orc.contiguous_f64_at(a, sfa, b, sfb, layout, rows, cols, abs_sum=True)
+    assert np.array_equal(bits_or_nan(val), full[np.ix_(rows, cols)])
+    full_abs = orc.m_grouped_fp8_gemm_nt_contiguous(_abs_codes(a), sfa, _abs_codes(b), sfb, layout,
+                                                    np.full((m, n), sentinel, np.uint16))
+    assert np.array_equal(bits_or_nan(mag), full_abs[np.ix_(rows, cols)])
+
+    # masked: counts 0, 1, max, clamped from above and below
+    g_count, max_m = 5, 40
+    a = _int_codes(rng, (g_count, max_m, k))
+    b = _int_codes(rng, (g_count, n, k))
+    sfa, sfb = _pow2(rng, (g_count, k // 128, max_m)), _pow2(rng, (g_count, n // 128, k // 128))
+    masked = np.array([0, 1, 40, 99, 17], np.int32)
+    d0 = np.full((g_count, max_m, n), sentinel, np.uint16)
+    full = orc.m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, masked, d0)
+    full_abs = orc.m_grouped_fp8_gemm_nt_masked(_abs_codes(a), sfa, _abs_codes(b), sfb, masked, d0)
+    rows = np.r_[0, 1, 2, 16, 17, 39]
+    for g in range(g_count):
+        val, mag = orc.masked_f64_at(a, sfa, b, sfb, masked, g, rows, cols, abs_sum=True)
+        assert np.array_equal(bits_or_nan(val), full[g][np.ix_(rows, cols)]), g
+        assert np.array_equal(bits_or_nan(mag), full_abs[g][np.ix_(rows, cols)]), g
+
+    # no-padding: unaligned groups, an empty one, rows no group owns
+    counts = np.array([5, 0, 130, 1, 60], np.int32)
+    m = 200
+    a, b = _int_codes(rng, (m, k)), _int_codes(rng, (5, n, k))
+    sfa, sfb = _pow2(rng, (k // 128, m)), _pow2(rng, (5, n // 128, k // 128))
+    full = orc.m_grouped_fp8_gemm_nt_nopad(a, sfa, b, sfb, counts, np.full((m, n), sentinel, np.uint16))
+    full_abs = orc.m_grouped_fp8_gemm_nt_nopad(_abs_codes(a), sfa, _abs_codes(b), sfb, counts,
+                                               np.full((m, n), sentinel, np.uint16))
+    rows = np.r_[0, 4, 5, 134, 135, 136, 137, 195, 196, 199]
+    val, mag = orc.nopad_f64_at(a, sfa, b, sfb, counts, rows, cols, abs_sum=True)
+    assert np.array_equal(bits_or_nan(val), full[np.ix_(rows, cols)])
+    assert np.array_equal(bits_or_nan(mag), full_abs[np.ix_(rows, cols)])
+
+    # K-grouped: per-row scales of both operands, an empty group, C
+    ks = [128, 0, 256, 384]
+    m, nk = 130, 260
+    a, b = _int_codes(rng, (m, sum(ks))), _int_codes(rng, (nk, sum(ks)))
+    sfa, sfb = _pow2(rng, (sum(ks) // 128, 132)), _pow2(rng, (sum(ks) // 128, 260))
+    c = rng.integers(-8, 9, size=(len(ks), m, nk)).astype(np.float64)
+    full = orc.k_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, ks, c)
+    full_abs = orc.k_grouped_fp8_gemm_nt_contiguous(_abs_codes(a), sfa, _abs_codes(b), sfb, ks, np.abs(c))
+    rows, kcols = np.r_[0, 1, 127, 128, 129], np.r_[0, 1, 127, 128, 200, 259]
+    for g in range(len(ks)):
+        val, mag = orc.k_grouped_f64_at(a, sfa, b, sfb, ks, g, rows, kcols, c, abs_sum=True)
+        assert np.array_equal(val, full[g][np.ix_(rows, kcols)]), g
+        assert np.array_equal(mag, full_abs[g][np.ix_(rows, kcols)]), g
+
+    # FP8 x FP4: one group of a masked batch
+    grid = np.array(sorted(E2M1_OF))
+    g_count, max_m, kf = 2, 20, 256
+    a = _int_codes(rng, (g_count, max_m, kf))
+    bvals = rng.choice(grid, size=(g_count, n, kf)) * rng.choice([-1.0, 1.0], size=(g_count, n, kf))
+    b = np.stack([_pack_e2m1(bvals[g]) for g in range(g_count)])
+    b_abs = np.stack([_pack_e2m1(np.abs(bvals[g])) for g in range(g_count)])
+    sfa, sfb = _pow2(rng, (g_count, kf // 128, max_m)), _pow2(rng, (g_count, kf // 32, n))
+    masked = np.array([20, 20], np.int32)
+    d0 = np.full((g_count, max_m, n), sentinel, np.uint16)
+    full = orc.m_grouped_fp8_fp4_gemm_nt_masked(a, sfa, b, sfb, masked, d0)
+    full_abs = orc.m_grouped_fp8_fp4_gemm_nt_masked(_abs_codes(a), sfa, b_abs, sfb, masked, d0)
+    rows = np.r_[0, 1, 18, 19]
+    for g in range(g_count):
+        val, mag = orc.fp8_fp4_f64_at(a[g], sfa[g], b[g], sfb[g], rows, cols, abs_sum=True)
+        assert np.array_equal(orc.bf16_bits(val), full[g][np.ix_(rows, cols)]), g
+        assert np.array_equal(orc.bf16_bits(mag), full_abs[g][np.ix_(rows, cols)]), g
+
+
 PINS = [
     pin_formats_golden,
     pin_near_tie_gemm,
     pin_exact_dense,
+    pin_exact_brute_force_matches,
     pin_exact_grouped,
     pin_integer_closed_form,
     pin_unit_scales_matmul,
@@ -611,6 +779,8 @@ PINS = [
     pin_fp4_element_positions,
     pin_exact_fp8_fp4,
     pin_fp4_matches_fp8_on_shared_values,
+    pin_contiguous_block_rule,
+    pin_sampled_functions_match_full,
 ]
 
 
@@ -640,7 +810,8 @@ def _mut_lhs_scale_first_row(mod):
 
 
 def _mut_rhs_scale_transposed(mod):
-    def f(b_codes, sfb):
+    def f(b_codes, sfb, rows=None):
+        b_codes = np.asarray(b_codes, np.uint8) if rows is None else np.asarray(b_codes, np.uint8)[rows]
         n, k = b_codes.shape
         v = mod.e4m3_decode_table()[b_codes]
         s = np.asarray(sfb, np.float64)
@@ -831,6 +1002,70 @@ def _mut_e2m1_bias_0(mod):
     mod.e2m1_decode_table = table
 
 
+def _mut_contiguous_any_valid_id(mod):
+    # every row with an id in [0, G) is computed, whatever its block's id
+    def f(layout, num_groups):
+        lay = np.asarray(layout, np.int64)
+        return np.where((lay >= 0) & (lay < num_groups), lay, -1)
+    mod.contiguous_row_groups = f
+
+
+def _mut_at_contiguous_wrong_group(mod):
+    # the sampled contiguous reference uses the next group's B
+    orig = mod.contiguous_f64_at
+
+    def f(a_codes, sfa, b_codes, sfb, layout, rows, cols, abs_sum=False):
+        return orig(a_codes, sfa, np.roll(b_codes, 1, axis=0), np.roll(sfb, 1, axis=0), layout, rows, cols, abs_sum)
+    mod.contiguous_f64_at = f
+
+
+def _mut_at_masked_off_by_one(mod):
+    orig = mod.masked_f64_at
+
+    def f(a_codes, sfa, b_codes, sfb, masked_m, group, rows, cols, abs_sum=False):
+        return orig(a_codes, sfa, b_codes, sfb, np.asarray(masked_m) + 1, group, rows, cols, abs_sum)
+    mod.masked_f64_at = f
+
+
+def _mut_at_nopad_shifted(mod):
+    # the sampled no-padding reference starts every group one row late
+    orig = mod.nopad_f64_at
+
+    def f(a_codes, sfa, b_codes, sfb, group_rows, rows, cols, abs_sum=False):
+        return orig(a_codes, sfa, b_codes, sfb, group_rows, np.asarray(rows) - 1, cols, abs_sum)
+    mod.nopad_f64_at = f
+
+
+def _mut_at_k_grouped_rhs_block_scales(mod):
+    # the sampled K-grouped reference reads the RHS scale of each 128-row block's first row
+    orig = mod.k_grouped_f64_at
+
+    def f(a_codes, sfa, b_codes, sfb, ks, group, rows, cols, c_init=None, abs_sum=False):
+        s = np.asarray(sfb)
+        s2 = np.repeat(s[:, ::128], 128, axis=1)[:, :s.shape[1]]
+        return orig(a_codes, sfa, b_codes, s2, ks, group, rows, cols, c_init, abs_sum)
+    mod.k_grouped_f64_at = f
+
+
+def _mut_at_fp4_nibbles_swapped(mod):
+    orig = mod.fp8_fp4_f64_at
+
+    def f(a_codes, sfa, b_packed_g, sfb_g, rows, cols, abs_sum=False):
+        p = np.asarray(b_packed_g, np.uint8)
+        return orig(a_codes, sfa, ((p >> 4) | (p << 4)).astype(np.uint8), sfb_g, rows, cols, abs_sum)
+    mod.fp8_fp4_f64_at = f
+
+
+def _mut_at_magnitude_of_sum(mod):
+    # |sum| instead of the sum of magnitudes for the error bound
+    orig = mod._rows_cols_f64
+
+    def f(a_codes, sfa, b_codes, sfb, rows, cols, abs_sum=False):
+        v = orig(a_codes, sfa, b_codes, sfb, rows, cols, False)
+        return (v, np.abs(v)) if abs_sum else v
+    mod._rows_cols_f64 = f
+
+
 MUTANTS = [
     _mut_lhs_scale_first_row,
     _mut_rhs_scale_transposed,
@@ -854,6 +1089,13 @@ MUTANTS = [
     _mut_e2m1_nibbles_swapped,
     _mut_fp4_scale_per_128,
     _mut_e2m1_bias_0,
+    _mut_contiguous_any_valid_id,
+    _mut_at_contiguous_wrong_group,
+    _mut_at_masked_off_by_one,
+    _mut_at_nopad_shifted,
+    _mut_at_k_grouped_rhs_block_scales,
+    _mut_at_fp4_nibbles_swapped,
+    _mut_at_magnitude_of_sum,
 ]
 
 
