@@ -93,10 +93,12 @@ dg_status dg_fp8_gemm_nt(const void* a, const float* sfa,
  *   b   [num_groups][n][k] E4M3          sfb [num_groups][n/128][k/128] float32
  *   d   [m][n] BF16
  *   grouped_layout [m] int32 (device): group id of each row, -1 for padding.
- * Row r of d is written iff grouped_layout[r] is the id g of the 128-row
- * block that holds r (the id of the block's first row) and 0 <= g < G.
- * Padding rows, and whole blocks whose first row has an id outside [0, G),
- * are never written and never influence written rows. m % 128 == 0.
+ * Row r of d is written iff grouped_layout[r] equals the id g of the first
+ * row of the 128-row block that holds r, and 0 <= g < G. Every other row
+ * (padding, an id outside [0, G), or an id that differs from its block's
+ * first row) is never written and never influences written rows; for
+ * layouts whose segments are 128-row aligned, as required, this writes
+ * exactly the rows with an id in [0, G). m % 128 == 0.
  */
 dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa,
                                               const void* b, const float* sfb,

@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdg.so")
 
-SOURCES = ["dg_kernel.hip", "dg_kernel_deep.hip", "dg_kernel_kgrouped.hip", "dg_kernel_fp4.hip", "dg_api.cpp"]
+SOURCES = ["dg_kernel.hip", "dg_kernel_deep.hip", "dg_kernel_kgrouped.hip", "dg_kernel_fp4.hip", "dg_ceiling.hip",
+           "dg_api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

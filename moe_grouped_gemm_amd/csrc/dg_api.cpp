@@ -18,13 +18,34 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int tma_aligned(int x, int esize) { return (x + (16 / esize) - 1) / (16 / esize) * (16 / esize); }
 
-// CU count of the current device, or 0 when there is none.
+// Per device: 0 = not yet queried, -1 = not a gfx950 (the kernels are built
+// for it only), else the CU count. Filled once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_cus[kMaxDevices];
+
+int query_device_cus(int dev) {
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return -1;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0 || (prop.gcnArchName[6] != '\0' && prop.gcnArchName[6] != ':'))
+    return -1;
+  return prop.multiProcessorCount > 0 ? prop.multiProcessorCount : -1;
+}
+
+// CU count of the current device, or 0 when there is none or it is not a
+// gfx950.
 int device_cus() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  return cus;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev >= kMaxDevices) {
+    const int c = query_device_cus(dev);
+    return c > 0 ? c : 0;
+  }
+  int c = g_device_cus[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    c = query_device_cus(dev);
+    g_device_cus[dev].store(c, std::memory_order_relaxed);
+  }
+  return c > 0 ? c : 0;
 }
 
 int effective_cus() {

@@ -76,6 +76,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// c + the 16x16 block of products of a and b summed over K = 128, OCP E4M3
+// operands without block scales: v_mfma_f32_16x16x128_f8f6f4. The compiler
+// exposes the f8f6f4 MFMAs only through the block-scaled builtin, and for
+// scale operands that are constant zero it selects this plain instruction
+// (no scale registers, checked in the generated code and by a CPU test of
+// the build) whose products are not scaled -- a scale code given in a
+// register would instead be applied as 2^(code - 127). The integer-exact
+// GPU tests, bit for bit against the oracle, pin that the products come out
+// unscaled.
+__device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// The same with E8M0 block scales: c + 2^(ea - 127) * 2^(eb - 127) * (the
+// products of a and b summed over K = 128), ea applied to the first
+// operand's row of each lane and eb to the second's.
+__device__ __forceinline__ f32x4 mfma_fp8_scaled(const i32x8& a, const i32x8& b, f32x4 c, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
+}
+
 // The E8M0 code of a float32 scale: its biased exponent field e, which the
 // MFMA's block-scale operand reads as 2^(e - 127) (e = 255: NaN). For a
 // positive normal power of two this is the scale itself; sign and mantissa
@@ -327,8 +347,8 @@ __device__ __forceinline__ TileRef next_active(const GemmArgs& p, int& t, int gr
   return none;
 }
 
-// Contiguous layout: which of a wave's 128 tile rows belong to the tile's
-// group. Lane l loads the group indices of rows wm0 + 2l and wm0 + 2l + 1 of
+// Contiguous layout: which of a wave's 128 tile rows are computed for the
+// tile's group. Lane l loads the group indices of rows wm0 + 2l and wm0 + 2l + 1 of
 // a tile one tile ahead of use (RowGroups); the K loop turns them into bit
 // masks (RowMask: bit l of `even` / `odd` is row 2l / 2l + 1) at a point
 // where the loads have landed long before, so that waiting for them does
@@ -342,6 +362,7 @@ struct RowMask {
 
 template <class C>
 __device__ __forceinline__ RowGroups load_row_groups(const GemmArgs& p, const TileRef& tr, int wm0, int lane) {
+  static_assert(C::WM == 128, "a wave's tile rows are exactly one 128-row block of the layout");
   RowGroups rg{-1, -1};
   const int r = tr.m0 + wm0 + 2 * lane;
   if (tr.active && r < p.m) rg.even = p.aux[r];
@@ -349,8 +370,15 @@ __device__ __forceinline__ RowGroups load_row_groups(const GemmArgs& p, const Ti
   return rg;
 }
 
+// The contiguous layout's row rule: a 128-row block belongs to the group
+// named by its first row's id, and a row of it is computed for that group
+// when the row's own id is the same (segments are aligned to 128 rows, so
+// in a well-formed layout every valid row passes). A wave's 128 rows are one
+// such block and lane 0's `even` row is its first row.
 __device__ __forceinline__ RowMask row_mask(const RowGroups& rg, int group) {
-  return RowMask{__builtin_amdgcn_ballot_w64(rg.even == group), __builtin_amdgcn_ballot_w64(rg.odd == group)};
+  const bool block_is_group = __builtin_amdgcn_readlane(rg.even, 0) == group;
+  return RowMask{__builtin_amdgcn_ballot_w64(block_is_group && rg.even == group),
+                 __builtin_amdgcn_ballot_w64(block_is_group && rg.odd == group)};
 }
 
 // Bits 0..7 of x moved to the even bit positions 0..14.

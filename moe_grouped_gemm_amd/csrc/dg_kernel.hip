@@ -393,14 +393,12 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const TileSrc& t0, c
           const int ea = e8m0_code(sav[mt % 4]);
 #pragma unroll
           for (int nt = 0; nt < C::NT; ++nt)
-            wt.acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[mt % 4], wt.acc[mt][nt],
-                                                                             0, 0, 0, eb, 0, ea);
+            wt.acc[mt][nt] = mfma_fp8_scaled(bf[nt], af[mt % 4], wt.acc[mt][nt], eb, ea);
         } else {
           f32x4 part[C::NT];
 #pragma unroll
           for (int nt = 0; nt < C::NT; ++nt)
-            part[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[mt % 4],
-                                                                       (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            part[nt] = mfma_fp8(bf[nt], af[mt % 4], (f32x4){0.f, 0.f, 0.f, 0.f});
           const float w = sav[mt % 4] * sb;
 #pragma unroll
           for (int nt = 0; nt < C::NT; ++nt) wt.acc[mt][nt] += part[nt] * w;
@@ -424,15 +422,11 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const TileSrc& t0, c
         f32x4 p6, p7;
         if constexpr (NB == C::MT) {
           if constexpr (E8) {
-            wt.acc[6][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[6 % 4], wt.acc[6][nt],
-                                                                            0, 0, 0, eb, 0, ea6);
-            wt.acc[7][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[7 % 4], wt.acc[7][nt],
-                                                                            0, 0, 0, eb, 0, ea7);
+            wt.acc[6][nt] = mfma_fp8_scaled(bf[nt], af[6 % 4], wt.acc[6][nt], eb, ea6);
+            wt.acc[7][nt] = mfma_fp8_scaled(bf[nt], af[7 % 4], wt.acc[7][nt], eb, ea7);
           } else {
-            p6 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[6 % 4], (f32x4){0.f, 0.f, 0.f, 0.f},
-                                                                 0, 0, 0, 0, 0, 0);
-            p7 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], af[7 % 4], (f32x4){0.f, 0.f, 0.f, 0.f},
-                                                                 0, 0, 0, 0, 0, 0);
+            p6 = mfma_fp8(bf[nt], af[6 % 4], (f32x4){0.f, 0.f, 0.f, 0.f});
+            p7 = mfma_fp8(bf[nt], af[7 % 4], (f32x4){0.f, 0.f, 0.f, 0.f});
           }
         }
         __builtin_amdgcn_sched_barrier(0);

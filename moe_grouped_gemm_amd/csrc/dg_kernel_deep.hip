@@ -396,13 +396,11 @@ __device__ __forceinline__ void band_mfmas(WaveTile<C>& wt, f32x4 (&part)[C::NT]
     const int ea = e8m0_code(o.sav[MT % 4]);
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt)
-      wt.acc[MT][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[MT % 4], wt.acc[MT][nt],
-                                                                       0, 0, 0, eb, 0, ea);
+      wt.acc[MT][nt] = mfma_fp8_scaled(o.bf[nt], o.af[MT % 4], wt.acc[MT][nt], eb, ea);
   } else {
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt)
-      part[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[MT % 4], (f32x4){0.f, 0.f, 0.f, 0.f},
-                                                                 0, 0, 0, 0, 0, 0);
+      part[nt] = mfma_fp8(o.bf[nt], o.af[MT % 4], (f32x4){0.f, 0.f, 0.f, 0.f});
   }
 }
 
@@ -463,15 +461,11 @@ __device__ __forceinline__ void step_on(WaveTile<C>& wt, Operands<C>& o, const S
   for (int nt = 0; nt < C::NT; ++nt) {
     f32x4 p6, p7;
     if constexpr (E8) {
-      wt.acc[6][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[6 % 4], wt.acc[6][nt],
-                                                                      0, 0, 0, eb, 0, ea6);
-      wt.acc[7][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[7 % 4], wt.acc[7][nt],
-                                                                      0, 0, 0, eb, 0, ea7);
+      wt.acc[6][nt] = mfma_fp8_scaled(o.bf[nt], o.af[6 % 4], wt.acc[6][nt], eb, ea6);
+      wt.acc[7][nt] = mfma_fp8_scaled(o.bf[nt], o.af[7 % 4], wt.acc[7][nt], eb, ea7);
     } else {
-      p6 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[6 % 4], (f32x4){0.f, 0.f, 0.f, 0.f},
-                                                           0, 0, 0, 0, 0, 0);
-      p7 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.bf[nt], o.af[7 % 4], (f32x4){0.f, 0.f, 0.f, 0.f},
-                                                           0, 0, 0, 0, 0, 0);
+      p6 = mfma_fp8(o.bf[nt], o.af[6 % 4], (f32x4){0.f, 0.f, 0.f, 0.f});
+      p7 = mfma_fp8(o.bf[nt], o.af[7 % 4], (f32x4){0.f, 0.f, 0.f, 0.f});
     }
     __builtin_amdgcn_sched_barrier(0);
     if (nt == 0) {

@@ -148,11 +148,9 @@ __device__ __forceinline__ void block(f32x4 (&acc)[MT][NT], const uint8_t* st, c
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       if constexpr (E8) {
-        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], a_cur, acc[mt][nt], 0, 0, 0, eb[nt], 0,
-                                                                      e8m0_code(s_cur));
+        acc[mt][nt] = mfma_fp8_scaled(bf[nt], a_cur, acc[mt][nt], eb[nt], e8m0_code(s_cur));
       } else {
-        const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[nt], a_cur, (f32x4){0.f, 0.f, 0.f, 0.f},
-                                                                           0, 0, 0, 0, 0, 0);
+        const f32x4 part = mfma_fp8(bf[nt], a_cur, (f32x4){0.f, 0.f, 0.f, 0.f});
         acc[mt][nt] += part * (sb[nt] * s_cur);
       }
     }

@@ -21,7 +21,7 @@ DG_OK = 0
 _STATUS_NAMES = {0: "DG_OK", 1: "DG_ERR_NULL", 2: "DG_ERR_SHAPE", 3: "DG_ERR_ALIGN",
                  4: "DG_ERR_UNSUPPORTED", 5: "DG_ERR_LAUNCH", 6: "DG_ERR_DEVICE"}
 
-# (name, argtypes, restype) of every symbol include/dg.h declares.
+# (name, argtypes, restype) of every symbol include/dg.h and include/dg_ceiling.h declare.
 _vp, _i = ctypes.c_void_p, ctypes.c_int
 SIGNATURES = [
     ("dg_fp8_gemm_nt", [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp], _i),
@@ -42,6 +42,7 @@ SIGNATURES = [
     ("dg_get_num_cus", [], _i),
     ("dg_set_num_cus", [_i], _i),
     ("dg_status_string", [_i], ctypes.c_char_p),
+    ("dg_mfma_fp8_ceiling", [_vp, _vp, _i, _i, ctypes.POINTER(ctypes.c_longlong), _vp], _i),
 ]
 
 _lib: Optional[ctypes.CDLL] = None

@@ -14,7 +14,7 @@ import torch
 
 from moe_grouped_gemm_amd import dg, synth
 from oracle import dg_oracle as O
-from parity import check_close, check_untouched
+from parity import abs_e4m3, check_close, check_untouched
 
 pytestmark = pytest.mark.gpu
 
@@ -45,13 +45,21 @@ DENSE_SHAPES = [
     (257, 128, 128),
     (64, 256, 4096),
     (1000, 640, 384),
-    (2048, 1024, 1024),  # more tiles than CUs
+    (2048, 1024, 1024),
+    (4096, 8192, 512),   # 512 tiles: two rounds of the persistent grid on 256 CUs
     (300, 896, 1024),    # N = 3.5 tiles
     (1, 896, 128),
     # K of 32 blocks and more: the deep-prefetch pipeline
     (300, 384, 4096),
     (257, 1792, 8192),
 ]
+
+
+def _dense_ref(a, sfa, b, sfb):
+    """The oracle's unrounded dense result and the sum of the products'
+    magnitudes (the oracle on |A| and |B|), for the per-element bound."""
+    return (O.gemm_nt_f64(a, sfa, b, sfb),
+            O.gemm_nt_f64(abs_e4m3(a), np.abs(sfa), abs_e4m3(b), np.abs(sfb)))
 
 
 @pytest.mark.parametrize("m,n,k", DENSE_SHAPES)
@@ -61,8 +69,8 @@ def test_dense_small(dev, m, n, k):
     d = w.new_output()
     dg.fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d)
     torch.cuda.synchronize()
-    ref = O.gemm_nt_f64(NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb))
-    check_close(NP(d), ref, f"dense {m}x{n}x{k}")
+    ref, mag = _dense_ref(NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb))
+    check_close(NP(d), ref, f"dense {m}x{n}x{k}", mag, k)
 
 
 CODE_OF = {0: 0x00, 1: 0x38, 2: 0x40, -1: 0xB8, -2: 0xC0}
@@ -118,16 +126,15 @@ def _contig_ref(w):
                                               np.full((w.m, w.n), 0xFFFF, np.uint16))
 
 
-def _check_contiguous(w, d, what):
+def _check_contiguous(w, d, what, sfa=None, sfb=None):
     got = NP(d)
     layout = NP(w.layout)
-    valid = layout >= 0
-    ref = np.full((w.m, w.n), np.nan)
-    for g in range(w.num_groups):
-        rows = np.nonzero(layout == g)[0]
-        if rows.size:
-            ref[rows] = O.dense_f64_at(NP(w.a), NP(w.sfa), NP(w.b)[g], NP(w.sfb)[g], rows, np.arange(w.n))
-    check_close(got[valid], ref[valid], what)
+    sfa = NP(w.sfa) if sfa is None else sfa
+    sfb = NP(w.sfb) if sfb is None else sfb
+    valid = O.contiguous_row_groups(layout, w.num_groups) >= 0
+    rows = np.nonzero(valid)[0]
+    ref, mag = O.contiguous_f64_at(NP(w.a), sfa, NP(w.b), sfb, layout, rows, np.arange(w.n), abs_sum=True)
+    check_close(got[valid], ref, what, mag, w.k)
     check_untouched(got[~valid], what + " padding rows")
 
 
@@ -167,9 +174,9 @@ def test_contiguous_out_of_range_ids_and_padding_blocks(dev):
     assert np.all(ref[256:] == 0xFFFF)
     valid = lay >= 0
     valid[256:] = False
-    ref64 = np.zeros((int(valid.sum()), w.n))
-    ref64[:] = O.dense_f64_at(NP(w.a), NP(w.sfa), NP(w.b)[0], NP(w.sfb)[0], np.nonzero(valid)[0], np.arange(w.n))
-    check_close(got[valid], ref64, "group 0")
+    ref64, mag = O.dense_f64_at(NP(w.a), NP(w.sfa), NP(w.b)[0], NP(w.sfb)[0], np.nonzero(valid)[0],
+                                np.arange(w.n), abs_sum=True)
+    check_close(got[valid], ref64, "group 0", mag, w.k)
 
 
 def test_contiguous_equals_dense_per_group(dev):
@@ -188,17 +195,104 @@ def test_contiguous_equals_dense_per_group(dev):
         start += r
 
 
+def test_contiguous_ids_changing_inside_blocks(dev):
+    """Layouts whose segments are not 128-row aligned: a row is written only
+    when its id is the id of its 128-row block's first row (and names a
+    group). Checked against the oracle's row rule and values, and rows it
+    leaves out must keep the sentinel."""
+    _say("contiguous ids changing inside 128-row blocks")
+    w = synth.make_contiguous([256, 256, 256], 384, 512, seed=41, device=dev)
+    lay = np.full(w.m, -1, np.int32)
+    lay[0:100] = 0
+    lay[100:128] = 1        # group 1 rows inside group 0's block
+    lay[128:200] = 1
+    lay[200:300] = 2        # crosses into block 2, whose first row says 2
+    lay[300:384] = 0        # group 0 rows inside group 2's block
+    lay[384] = -1           # block 3 starts with padding
+    lay[385:500] = 1
+    lay[512:640] = 2        # an aligned block in the second 256-row tile
+    lay[640:700] = 9        # an id outside [0, G)
+    w.layout.copy_(torch.from_numpy(lay))
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout)
+    torch.cuda.synchronize()
+    owner = O.contiguous_row_groups(lay, w.num_groups)
+    assert np.array_equal(np.nonzero(owner >= 0)[0], np.r_[0:100, 128:200, 256:300, 512:640])
+    _check_contiguous(w, d, "contiguous unaligned ids")
+    ref_bits = O.m_grouped_fp8_gemm_nt_contiguous(NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb), lay,
+                                                  np.full((w.m, w.n), 0xFFFF, np.uint16))
+    assert np.all(ref_bits[owner < 0] == 0xFFFF)
+
+
+def _int_exact_grouped(g_count, rows_a, n, k, seed):
+    """Integer-exact operands for grouped layouts: codes in {-2..2}, B per
+    group, power-of-two scales varying per K block, row and N block."""
+    a, sfa, _, _ = _int_exact(rows_a, 128, k, seed)
+    bs, sfbs = [], []
+    for g in range(g_count):
+        _, _, b, sfb = _int_exact(4, n, k, seed + 100 + g)
+        bs.append(b)
+        sfbs.append(sfb)
+    return a, sfa, np.stack(bs), np.stack(sfbs)
+
+
+@pytest.mark.parametrize("k", [1024, 4096])
+def test_grouped_integer_exact_bitwise(dev, k):
+    """Contiguous, masked and no-padding layouts with integer-exact inputs:
+    every float32 intermediate is exact, so D equals the oracle bit for bit
+    (K = 4096 runs the deep-prefetch pipeline)."""
+    _say(f"grouped integer-exact k={k}")
+    n = 384
+    # contiguous: groups of 200, 0, 77 and 300 rows, each padded to 128
+    rows = [200, 0, 77, 300]
+    layout = synth.contiguous_layout(rows)
+    m = layout.size
+    a, sfa, b, sfb = _int_exact_grouped(len(rows), m, n, k, seed=k)
+    d = synth.sentinel_output((m, n), dev)
+    dg.m_grouped_fp8_gemm_nt_contiguous(_dev_fp8(a, dev), torch.from_numpy(sfa).to(dev), _dev_fp8(b, dev),
+                                        torch.from_numpy(sfb).to(dev), d, torch.from_numpy(layout).to(dev))
+    torch.cuda.synchronize()
+    ref = O.m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, layout, np.full((m, n), 0xFFFF, np.uint16))
+    assert np.array_equal(NP(d), ref), f"contiguous: {np.sum(NP(d) != ref)} mismatching elements"
+    # no-padding: the same rows without padding, and 9 rows no group owns
+    m2 = sum(rows) + 9
+    a2, sfa2, b2, sfb2 = _int_exact_grouped(len(rows), m2, n, k, seed=k + 1)
+    counts = np.array(rows, np.int32)
+    d = synth.sentinel_output((m2, n), dev)
+    dg.m_grouped_fp8_gemm_nt_nopad(_dev_fp8(a2, dev), torch.from_numpy(sfa2).to(dev), _dev_fp8(b2, dev),
+                                   torch.from_numpy(sfb2).to(dev), d, torch.from_numpy(counts).to(dev))
+    torch.cuda.synchronize()
+    ref = O.m_grouped_fp8_gemm_nt_nopad(a2, sfa2, b2, sfb2, counts, np.full((m2, n), 0xFFFF, np.uint16))
+    assert np.array_equal(NP(d), ref), f"nopad: {np.sum(NP(d) != ref)} mismatching elements"
+    # masked: counts below, at and past the 64-row band boundaries
+    masked = np.array([1, 64, 65, 200, 0, 256], np.int32)
+    g_count, max_m = masked.size, 256
+    a3, _, b3, sfb3 = _int_exact_grouped(g_count, g_count * max_m, n, k, seed=k + 2)
+    a3 = a3.reshape(g_count, max_m, k)
+    rng = np.random.default_rng(k)
+    sfa3 = np.ldexp(1.0, rng.integers(-2, 3, size=(g_count, k // 128, max_m))).astype(np.float32)
+    d = synth.sentinel_output((g_count, max_m, n), dev)
+    dg.m_grouped_fp8_gemm_nt_masked(_dev_fp8(a3, dev), torch.from_numpy(sfa3).to(dev), _dev_fp8(b3, dev),
+                                    torch.from_numpy(sfb3).to(dev), d, torch.from_numpy(masked).to(dev))
+    torch.cuda.synchronize()
+    ref = O.m_grouped_fp8_gemm_nt_masked(a3, sfa3, b3, sfb3, masked, np.full((g_count, max_m, n), 0xFFFF, np.uint16))
+    assert np.array_equal(NP(d), ref), f"masked: {np.sum(NP(d) != ref)} mismatching elements"
+
+
 # ---------------------------------------------------------------------------
 # Masked layout
 # ---------------------------------------------------------------------------
 
-def _check_masked(w, d, counts, what):
+def _check_masked(w, d, counts, what, sfa=None, sfb=None):
     got = NP(d)
+    sfa = NP(w.sfa) if sfa is None else sfa
+    sfb = NP(w.sfb) if sfb is None else sfb
     for g, c in enumerate(counts):
         v = min(max(int(c), 0), w.max_m)
         if v:
-            ref = O.dense_f64_at(NP(w.a)[g], NP(w.sfa)[g], NP(w.b)[g], NP(w.sfb)[g], np.arange(v), np.arange(w.n))
-            check_close(got[g, :v], ref, f"{what} group {g}")
+            ref, mag = O.dense_f64_at(NP(w.a)[g], sfa[g], NP(w.b)[g], sfb[g], np.arange(v), np.arange(w.n),
+                                      abs_sum=True)
+            check_close(got[g, :v], ref, f"{what} group {g}", mag, w.k)
         check_untouched(got[g, v:], f"{what} group {g} rows >= {v}")
 
 
@@ -296,14 +390,16 @@ def test_masked_partial_band_copies(dev, ue8m0):
 # No-padding layout
 # ---------------------------------------------------------------------------
 
-def _check_nopad(w, d, what):
+def _check_nopad(w, d, what, sfa=None, sfb=None):
     got = NP(d)
+    sfa = NP(w.sfa) if sfa is None else sfa
+    sfb = NP(w.sfb) if sfb is None else sfb
     owned = np.zeros(w.m, bool)
     for g, (first, end) in enumerate(O.nopad_row_ranges(NP(w.group_rows), w.m)):
         if end > first:
-            ref = O.dense_f64_at(NP(w.a), NP(w.sfa), NP(w.b)[g], NP(w.sfb)[g], np.arange(first, end),
-                                 np.arange(w.n))
-            check_close(got[first:end], ref, f"{what} group {g}")
+            ref, mag = O.dense_f64_at(NP(w.a), sfa, NP(w.b)[g], sfb[g], np.arange(first, end), np.arange(w.n),
+                                      abs_sum=True)
+            check_close(got[first:end], ref, f"{what} group {g}", mag, w.k)
             owned[first:end] = True
     check_untouched(got[~owned], what + " rows no group owns")
 
@@ -410,8 +506,8 @@ def test_ue8m0_dense(dev, m, n, k):
     d = w.new_output()
     dg.fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d, ue8m0=True)
     torch.cuda.synchronize()
-    ref = O.gemm_nt_f64(NP(w.a), O.e8m0_value(NP(w.sfa)), NP(w.b), O.e8m0_value(NP(w.sfb)))
-    check_close(NP(d), ref, f"ue8m0 dense {m}x{n}x{k}")
+    ref, mag = _dense_ref(NP(w.a), O.e8m0_value(NP(w.sfa)), NP(w.b), O.e8m0_value(NP(w.sfb)))
+    check_close(NP(d), ref, f"ue8m0 dense {m}x{n}x{k}", mag, k)
 
 
 @pytest.mark.parametrize("m,n,k", [(200, 256, 1024), (77, 896, 512), (65, 256, 4096)])
@@ -436,20 +532,20 @@ def test_ue8m0_grouped_layouts(dev, k):
     d = w.new_output()
     dg.m_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout, ue8m0=True)
     torch.cuda.synchronize()
-    _check_contiguous(w, d, "ue8m0 contiguous")
+    _check_contiguous(w, d, "ue8m0 contiguous", O.e8m0_value(NP(w.sfa)), O.e8m0_value(NP(w.sfb)))
     counts = [0, 1, 200, 77]
     w = synth.make_masked(counts, 200, 256, k, seed=22, device=dev, poison_invalid=True, ue8m0=True)
     _assert_pow2(w.sfa, w.sfb)
     d = w.new_output()
     dg.m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m, ue8m0=True)
     torch.cuda.synchronize()
-    _check_masked(w, d, counts, "ue8m0 masked")
+    _check_masked(w, d, counts, "ue8m0 masked", O.e8m0_value(NP(w.sfa)), O.e8m0_value(NP(w.sfb)))
     w = synth.make_nopad(rows, 256, k, seed=23, device=dev, tail=7, poison_tail=True, ue8m0=True)
     _assert_pow2(w.sfa, w.sfb)
     d = w.new_output()
     dg.m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows, ue8m0=True)
     torch.cuda.synchronize()
-    _check_nopad(w, d, "ue8m0 nopad")
+    _check_nopad(w, d, "ue8m0 nopad", O.e8m0_value(NP(w.sfa)), O.e8m0_value(NP(w.sfb)))
 
 
 def test_ue8m0_drops_mantissa(dev):
@@ -464,8 +560,8 @@ def test_ue8m0_drops_mantissa(dev):
     dg.fp8_gemm_nt(w.a, floor_sfa, w.b, floor_sfb, d2, ue8m0=True)
     torch.cuda.synchronize()
     assert torch.equal(d1.view(torch.int16), d2.view(torch.int16))
-    ref = O.gemm_nt_f64(NP(w.a), O.e8m0_value(NP(w.sfa)), NP(w.b), O.e8m0_value(NP(w.sfb)))
-    check_close(NP(d1), ref, "ue8m0 mantissa dropped")
+    ref, mag = _dense_ref(NP(w.a), O.e8m0_value(NP(w.sfa)), NP(w.b), O.e8m0_value(NP(w.sfb)))
+    check_close(NP(d1), ref, "ue8m0 mantissa dropped", mag, w.k)
 
 
 def test_ue8m0_close_to_float32_path(dev):
@@ -484,9 +580,14 @@ def test_ue8m0_close_to_float32_path(dev):
 # ---------------------------------------------------------------------------
 
 def _fp4_ref_rows(w, g, rows, cols, a=None, sfa=None):
+    """(value, magnitude) of group g's W4A8 result at rows x cols."""
     a = NP(w.a) if a is None else a
     sfa = NP(w.sfa) if sfa is None else sfa
-    return O.fp8_fp4_f64_at(a, sfa, NP(w.b)[g], NP(w.sfb)[g], rows, cols)
+    return O.fp8_fp4_f64_at(a, sfa, NP(w.b)[g], NP(w.sfb)[g], rows, cols, abs_sum=True)
+
+
+def _check_fp4(got, refmag, what, k):
+    check_close(got, refmag[0], what, refmag[1], k)
 
 
 @pytest.mark.parametrize("rows,n,k", [([130, 0, 77, 256, 1], 256, 512), ([5, 300, 1, 129], 384, 1024),
@@ -501,7 +602,7 @@ def test_fp8_fp4_contiguous_small(dev, rows, n, k):
     for g in range(w.num_groups):
         idx = np.nonzero(layout == g)[0]
         if idx.size:
-            check_close(got[idx], _fp4_ref_rows(w, g, idx, np.arange(w.n)), f"w4a8 contiguous group {g}")
+            _check_fp4(got[idx], _fp4_ref_rows(w, g, idx, np.arange(w.n)), f"w4a8 contiguous group {g}", k)
     check_untouched(got[layout < 0], "w4a8 contiguous padding rows")
     ref_bits = O.m_grouped_fp8_fp4_gemm_nt_contiguous(NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb), layout,
                                                       np.full((w.m, w.n), 0xFFFF, np.uint16))
@@ -519,17 +620,19 @@ def test_fp8_fp4_masked_small(dev, counts, max_m, n, k):
     for g, c in enumerate(counts):
         v = min(max(int(c), 0), max_m)
         if v:
-            check_close(got[g, :v], _fp4_ref_rows(w, g, np.arange(v), np.arange(n), NP(w.a)[g], NP(w.sfa)[g]),
-                        f"w4a8 masked group {g}")
+            _check_fp4(got[g, :v], _fp4_ref_rows(w, g, np.arange(v), np.arange(n), NP(w.a)[g], NP(w.sfa)[g]),
+                       f"w4a8 masked group {g}", k)
         check_untouched(got[g, v:], f"w4a8 masked group {g} rows >= {v}")
 
 
 def test_fp8_fp4_masked_partial_band_copies(dev):
-    """Valid rows ending at and next to the 64-row boundary of each wave's 128
-    rows (below it the wave runs the K loop copy without bands 4-7), with
-    three workgroups taking all tiles so that both copies alternate in one
-    workgroup."""
-    counts = [64, 65, 192, 193, 48, 80, 16, 17, 256, 0, 1, 129]
+    """Valid rows ending at and next to the 32-, 64- and 96-row boundaries of
+    each wave's 128 rows: a wave whose rows lie in its first 2, 4 or 6 bands
+    runs the K loop copy without the other bands' MFMAs, and each copy is run
+    with its last band valid (32, 64, 96; 160, 192, 224 for the second wave)
+    and with one row past it. Three workgroups take all tiles so that the
+    copies alternate in one workgroup."""
+    counts = [32, 33, 64, 65, 96, 97, 160, 161, 192, 193, 224, 225, 48, 80, 16, 17, 256, 0, 1, 129]
     _say("w4a8 masked partial bands")
     w = synth.make_masked(counts, 256, 512, 640, seed=37, device=dev, poison_invalid=True, fp4=True)
     d = w.new_output()
@@ -543,9 +646,38 @@ def test_fp8_fp4_masked_partial_band_copies(dev):
     for g, c in enumerate(counts):
         v = min(max(int(c), 0), 256)
         if v:
-            check_close(got[g, :v], _fp4_ref_rows(w, g, np.arange(v), np.arange(512), NP(w.a)[g], NP(w.sfa)[g]),
-                        f"w4a8 masked partial bands group {g}")
+            _check_fp4(got[g, :v], _fp4_ref_rows(w, g, np.arange(v), np.arange(512), NP(w.a)[g], NP(w.sfa)[g]),
+                       f"w4a8 masked partial bands group {g}", 640)
         check_untouched(got[g, v:], f"w4a8 masked partial bands group {g} rows >= {v}")
+
+
+@pytest.mark.parametrize("k", [128, 1024])
+def test_fp8_fp4_float32_scales(dev, k):
+    """FP32 logical scales that are not powers of two: each is taken as its
+    E8M0 value (the float32 exponent field), for the LHS 1x128 and the RHS
+    1x32 scales alike. The output equals the call on the scales rounded down
+    to powers of two bit for bit, and the oracle within the tolerance; the
+    page's adapted case is K = 128."""
+    _say(f"w4a8 float32 scales k={k}")
+    w = synth.make_contiguous([130, 77, 256], 256, k, seed=k + 43, device=dev, fp4=True)
+    rng = np.random.default_rng(k)
+    sfa = NP(w.sfa) * rng.uniform(1.0, 2.0, size=NP(w.sfa).shape).astype(np.float32)
+    sfb = NP(w.sfb) * rng.uniform(1.0, 2.0, size=NP(w.sfb).shape).astype(np.float32)
+    assert not np.array_equal(O.e8m0_value(sfb[sfb != 0]), sfb[sfb != 0].astype(np.float64))
+    d1, d2 = w.new_output(), w.new_output()
+    dg.m_grouped_fp8_fp4_gemm_nt_contiguous(w.a, torch.from_numpy(sfa).to(dev), w.b, torch.from_numpy(sfb).to(dev),
+                                            d1, w.layout)
+    floor_a = torch.from_numpy(O.e8m0_value(sfa).astype(np.float32)).to(dev)
+    floor_b = torch.from_numpy(O.e8m0_value(sfb).astype(np.float32)).to(dev)
+    dg.m_grouped_fp8_fp4_gemm_nt_contiguous(w.a, floor_a, w.b, floor_b, d2, w.layout)
+    torch.cuda.synchronize()
+    assert torch.equal(d1.view(torch.int16), d2.view(torch.int16))
+    got, layout = NP(d1), NP(w.layout)
+    for g in range(w.num_groups):
+        idx = np.nonzero(layout == g)[0]
+        ref = O.fp8_fp4_f64_at(NP(w.a), sfa, NP(w.b)[g], sfb[g], idx, np.arange(w.n), abs_sum=True)
+        _check_fp4(got[idx], ref, f"w4a8 float32 scales group {g}", k)
+    check_untouched(got[layout < 0], "w4a8 float32 scales padding rows")
 
 
 def test_fp8_fp4_integer_exact_bitwise(dev):
@@ -587,7 +719,7 @@ def test_fp8_fp4_integer_exact_bitwise(dev):
 # Frobenius error must stay below 5e-5 (measured: 1.35e-5).
 
 def _check_k_grouped(w, d, c0, what, groups=None, rows=None, cols=None):
-    got = d.detach().cpu().numpy().astype(np.float64)
+    got = d.detach().cpu().numpy()                       # float32 [G, M, N]
     c_np = None if c0 is None else c0.detach().cpu().numpy()
     rows = np.arange(w.m) if rows is None else rows
     cols = np.arange(w.n) if cols is None else cols
@@ -596,8 +728,8 @@ def _check_k_grouped(w, d, c0, what, groups=None, rows=None, cols=None):
         sfa, sfb = O.e8m0_value(sfa), O.e8m0_value(sfb)
     for g in (range(w.num_groups) if groups is None else groups):
         ref, mag = O.k_grouped_f64_at(a, sfa, b, sfb, w.ks, g, rows, cols, c_np, abs_sum=True)
-        cmag = 0.0 if c_np is None else np.abs(c_np[g][np.ix_(rows, cols)])
-        out = got[g][np.ix_(rows, cols)]
+        cmag = 0.0 if c_np is None else np.abs(c_np[g][np.ix_(rows, cols)].astype(np.float64))
+        out = got[g][np.ix_(rows, cols)].astype(np.float64)
         nkb = w.ks[g] // 128
         bound = (2.0 ** -15 + (nkb + 3) * 2.0 ** -24) * (mag - cmag) + 2.0 ** -24 * cmag + 1e-30
         bad = np.abs(out - ref) > bound
@@ -659,13 +791,31 @@ def test_k_grouped_many_groups(dev):
 
 
 # ---------------------------------------------------------------------------
-# The benchmark workloads at full size (sampled comparison)
+# The benchmark workloads at full size: every valid element
 # ---------------------------------------------------------------------------
+#
+# The oracle runs group by group in chunks of rows: each group's RHS is
+# dequantised once (dequant_rhs, or dequant_rhs_e2m1 for FP4), each chunk's
+# LHS rows with dequant_lhs, and the float64 products give the reference and
+# the magnitudes for the per-element bound. Every row no group owns is
+# checked against the sentinel.
 
-def _sample(n_total, count, rng, extra=()):
-    idx = set(int(x) for x in rng.choice(n_total, size=min(count, n_total), replace=False))
-    idx.update(int(e) for e in extra if 0 <= e < n_total)
-    return np.array(sorted(idx), dtype=np.int64)
+ROW_CHUNK = 2048
+
+
+def _check_rows_full(got, a, sfa_v, bhat, rows, k, what):
+    babs = np.abs(bhat)
+    for i in range(0, rows.size, ROW_CHUNK):
+        r = rows[i:i + ROW_CHUNK]
+        ahat = O.dequant_lhs(a[r], sfa_v[:, r])
+        check_close(got[r], ahat @ bhat.T, f"{what} rows {r[0]}..{r[-1]}", np.abs(ahat) @ babs.T, k)
+
+
+def _rhs(w, g, sfb_v):
+    b = NP(w.b)
+    if getattr(w, "fp4", False):
+        return O.dequant_rhs_e2m1(b[g], sfb_v[g])
+    return O.dequant_rhs(b[g], sfb_v[g])
 
 
 @pytest.mark.parametrize("index", list(range(synth.NUM_WORKLOADS)))
@@ -677,67 +827,39 @@ def test_workload_full_size(dev, index):
     c0 = d.clone() if spec.kind == "k_grouped" else None
     dg.run_workload(w, d)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(100 + index)
-    if getattr(w, "fp4", False):
-        got = NP(d)
-        if spec.kind == "contiguous":
-            layout = NP(w.layout)
-            cols = _sample(w.n, 48, rng, (0, 127, 128, w.n - 1))
-            for g in range(w.num_groups):
-                idx = np.nonzero(layout == g)[0]
-                rows = idx[_sample(idx.size, 12, rng, (0, idx.size - 1))]
-                check_close(got[np.ix_(rows, cols)], _fp4_ref_rows(w, g, rows, cols), f"{spec.name} group {g}")
-            check_untouched(got[layout < 0], spec.name + " padding rows")
-        else:
-            for g in range(w.num_groups):
-                v = w.counts[g]
-                rows = _sample(v, 8, rng, (0, v - 1))
-                cols = _sample(w.n, 32, rng, (0, w.n - 1))
-                ref = _fp4_ref_rows(w, g, rows, cols, NP(w.a)[g], NP(w.sfa)[g])
-                check_close(got[g][np.ix_(rows, cols)], ref, f"{spec.name} group {g}")
-                check_untouched(got[g, v:], f"{spec.name} group {g} rows >= {v}")
-        return
     if spec.kind == "k_grouped":
-        rows = _sample(w.m, 24, rng, (0, 255, 256, w.m - 1))
-        cols = _sample(w.n, 24, rng, (0, 255, 256, w.n - 1))
-        _check_k_grouped(w, d, c0, spec.name, rows=rows, cols=cols)
+        _check_k_grouped(w, d, c0, spec.name)
         return
     got = NP(d)
-    a, sfa, b, sfb = NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb)
-    if w.ue8m0:
-        sfa, sfb = O.e8m0_value(sfa), O.e8m0_value(sfb)
+    a, sfa, sfb = NP(w.a), NP(w.sfa), NP(w.sfb)
+    fp4 = getattr(w, "fp4", False)
+    # The W4A8 calls read every scale as E8M0, as do the *_ue8m0 calls; the
+    # FP4 RHS scales are decoded inside dequant_rhs_e2m1.
+    sfa_v = O.e8m0_value(sfa) if (w.ue8m0 or fp4) else sfa
+    sfb_v = O.e8m0_value(sfb) if (w.ue8m0 and not fp4) else sfb
+    k = w.k
     if spec.kind == "dense":
-        rows = _sample(w.m, 96, rng, (0, 127, 128, 255, 256, w.m - 1))
-        cols = _sample(w.n, 96, rng, (0, 127, 128, 255, w.n - 1))
-        ref = O.dense_f64_at(a, sfa, b, sfb, rows, cols)
-        check_close(got[np.ix_(rows, cols)], ref, spec.name)
+        _check_rows_full(got, a, sfa_v, O.dequant_rhs(NP(w.b), sfb_v), np.arange(w.m), k, spec.name)
     elif spec.kind == "contiguous":
-        layout = NP(w.layout)
-        valid_rows = np.nonzero(layout >= 0)[0]
-        starts = np.nonzero(np.diff(np.r_[-2, layout]) != 0)[0]
-        rows = np.union1d(valid_rows[rng.choice(valid_rows.size, 128, replace=False)],
-                          np.intersect1d(starts, valid_rows))
-        cols = _sample(w.n, 64, rng, (0, 127, 128, w.n - 1))
-        ref = O.contiguous_f64_at(a, sfa, b, sfb, layout, rows, cols)
-        check_close(got[np.ix_(rows, cols)], ref, spec.name)
-        check_untouched(got[layout < 0], spec.name + " padding rows")
-    elif spec.kind == "nopad":
-        group_rows = NP(w.group_rows)
-        ranges = O.nopad_row_ranges(group_rows, w.m)
-        firsts = [f for f, e in ranges if e > f]
-        lasts = [e - 1 for f, e in ranges if e > f]
-        rows = _sample(w.m, 128, rng, firsts + lasts)
-        cols = _sample(w.n, 64, rng, (0, 127, 128, w.n - 1))
-        ref = O.nopad_f64_at(a, sfa, b, sfb, group_rows, rows, cols)
-        check_close(got[np.ix_(rows, cols)], ref, spec.name)
-        used = max(lasts) + 1
-        check_untouched(got[used:], spec.name + " rows no group owns")
-    else:
-        counts = w.counts
+        owner = O.contiguous_row_groups(NP(w.layout), w.num_groups)
         for g in range(w.num_groups):
-            v = counts[g]
-            rows = _sample(v, 8, rng, (0, v - 1))
-            cols = _sample(w.n, 32, rng, (0, w.n - 1))
-            ref = O.masked_f64_at(a, sfa, b, sfb, w.masked_m.cpu().numpy(), g, rows, cols)
-            check_close(got[g][np.ix_(rows, cols)], ref, f"{spec.name} group {g}")
+            rows = np.nonzero(owner == g)[0]
+            if rows.size:
+                _say(f"  group {g}: {rows.size} rows")
+                _check_rows_full(got, a, sfa_v, _rhs(w, g, sfb_v), rows, k, f"{spec.name} group {g}")
+        check_untouched(got[owner < 0], spec.name + " padding rows")
+    elif spec.kind == "nopad":
+        owned = np.zeros(w.m, bool)
+        for g, (first, end) in enumerate(O.nopad_row_ranges(NP(w.group_rows), w.m)):
+            if end > first:
+                _say(f"  group {g}: rows {first}..{end - 1}")
+                _check_rows_full(got, a, sfa_v, _rhs(w, g, sfb_v), np.arange(first, end), k, f"{spec.name} group {g}")
+                owned[first:end] = True
+        check_untouched(got[~owned], spec.name + " rows no group owns")
+    else:
+        for g in range(w.num_groups):
+            v = min(max(int(w.counts[g]), 0), w.max_m)
+            if v:
+                _check_rows_full(got[g], a[g], sfa_v[g], _rhs(w, g, sfb_v), np.arange(v), k,
+                                 f"{spec.name} group {g}")
             check_untouched(got[g, v:], f"{spec.name} group {g} rows >= {v}")
