@@ -10,6 +10,8 @@ JSON line.
                     [--no-cpu-baseline] [--no-extra] [--copy-calibration]
 
 --only INDEX times a single workload (0..12), for profiling runs.
+Before the W warm-up steps, about 0.25 s of untimed calls let the GPU
+clocks settle (a GEMM on random data runs the part below its nominal clock).
 Besides the back-to-back timing, every workload is also timed cold: before
 each of --cold-iters calls a 1 GiB scratch buffer is read, which evicts the
 L2 caches and the 256 MB Infinity Cache, and each call is timed on its own
@@ -57,6 +59,7 @@ def parse_args():
     p.add_argument("--no-extra", action="store_true")
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--cold-iters", type=int, default=30)
+    p.add_argument("--no-ceiling", action="store_true")
     return p.parse_args()
 
 
@@ -95,11 +98,31 @@ def read_traffic(spec):
         return None
 
 
+SETTLE_S = 0.25   # untimed GPU work before the warm-up steps
+
+
+def settle(w, d):
+    """Untimed calls for about SETTLE_S seconds of GPU time, so that the
+    clocks have ramped before the timed steps."""
+    import torch
+    from moe_grouped_gemm_amd import dg
+
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(20):
+            dg.run_workload(w, d)
+        torch.cuda.synchronize()
+        n += 20
+    return n
+
+
 def time_workload(w, steps: int, warmup: int):
     import torch
     from moe_grouped_gemm_amd import dg
 
     d = w.new_output()
+    settle(w, d)
     for _ in range(warmup):
         dg.run_workload(w, d)
     torch.cuda.synchronize()
@@ -164,6 +187,42 @@ def copy_ceiling_gbs(buf) -> float:
     return 2 * buf.numel() * buf.element_size() / (ms * 1e-3) / 1e9
 
 
+def mfma_ceiling_tflops(variant: int, iters: int = 4096) -> float:
+    """FP8 dense TFLOP/s of the matrix-core loop alone (dg_mfma_fp8_ceiling:
+    the GEMM kernels' launch shape and MFMA on random E4M3 operands, nothing
+    else), median of 5 timed launches after 3 untimed ones."""
+    import ctypes
+    import statistics
+    import torch
+    from moe_grouped_gemm_amd import dg
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12345)
+    frag = torch.randint(0, 256, (4096,), dtype=torch.uint8, device="cuda", generator=g)
+    frag[(frag & 0x7F) == 0x7F] = 0x3C          # no NaN codes
+    sink = torch.empty(512 * max(dg.get_num_cus(), 1), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    flops = ctypes.c_longlong(0)
+
+    def launch():
+        st = dg.lib().dg_mfma_fp8_ceiling(frag.data_ptr(), sink.data_ptr(), iters, variant,
+                                          ctypes.byref(flops), ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"dg_mfma_fp8_ceiling: status {st}")
+    for _ in range(3):
+        launch()
+    times = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        launch()
+        b.record(stream)
+        times.append((a, b))
+    torch.cuda.synchronize()
+    ms = statistics.median(x.elapsed_time(y) for x, y in times)
+    return flops.value / (ms * 1e-3) / 1e12
+
+
 def inputs_sha256(w) -> str:
     """SHA-256 (first 16 hex digits) of a workload's quantised operand and
     scale bytes, so that runs on different machines can be matched."""
@@ -174,37 +233,56 @@ def inputs_sha256(w) -> str:
     return h.hexdigest()[:16]
 
 
+def blas_threads_to_use() -> tuple:
+    """(affinity-mask cores, BLAS threads to use): the threads are the cores
+    of the process affinity mask, but no more than OMP_NUM_THREADS when the
+    environment sets it (a host shared between GPUs gives each its share)."""
+    affinity = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    threads = min(affinity, int(env)) if env and env.isdigit() and int(env) > 0 else affinity
+    return affinity, threads
+
+
 def cpu_baseline(w, budget_s: float = 20.0):
     """The oracle timed on this host on the same bytes (full workload,
-    repeated while within the time budget)."""
+    repeated while within the time budget), with the BLAS thread count set
+    explicitly; plus the exact-rational brute force timed once on a tiny
+    shape on one core."""
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
     from moe_grouped_gemm_amd import synth
     from oracle import dg_oracle as O
 
+    affinity, threads = blas_threads_to_use()
     a, sfa, b, sfb = (synth.to_numpy_bytes(t) for t in (w.a, w.sfa, w.b, w.sfb))
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-        if infos:
-            threads = int(infos[0]["num_threads"])
-    except Exception:
-        pass
-    # About 10 s of CPU work: repeat the full workload while under half the budget.
-    runs, t_total = 0, 0.0
-    while runs == 0 or (t_total < budget_s / 2 and runs < 40):
-        t0 = time.perf_counter()
-        O.fp8_gemm_nt(a, sfa, b, sfb)
-        t_total += time.perf_counter() - t0
-        runs += 1
+    with threadpool_limits(limits=threads, user_api="blas"):
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        used = int(blas[0]["num_threads"]) if blas else threads
+        vendor = (f"{blas[0].get('internal_api')} {blas[0].get('version')}" if blas else "unknown")
+        # About 10 s of CPU work: repeat the full workload while under half the budget.
+        runs, t_total = 0, 0.0
+        while runs == 0 or (t_total < budget_s / 2 and runs < 40):
+            t0 = time.perf_counter()
+            O.fp8_gemm_nt(a, sfa, b, sfb)
+            t_total += time.perf_counter() - t0
+            runs += 1
     sec = t_total / runs
+    # exact rationals, single core, on 2 x 128 x 256 of the same workload's bytes
+    tm, tn, tk = 2, 128, 256
+    t0 = time.perf_counter()
+    O.gemm_nt_exact(a[:tm, :tk], sfa[:tk // 128, :tm], b[:tn, :tk], sfb[:1, :tk // 128])
+    exact_s = time.perf_counter() - t0
     return {
         "value": round(w.flops() / sec / 1e12, 6),
         "unit": "TFLOPS",
-        "cores": threads if threads else len(os.sched_getaffinity(0)),
+        "cores": used,
         "kind": "oracle",
         "sample": f"full {w.m}x{w.n}x{w.k} dense workload, {runs} run(s) of the float64 numpy oracle "
                   f"(dequantise, fp64 GEMM, BF16 rounding), {sec:.2f} s each",
+        "affinity_cores": affinity,
+        "blas": vendor,
+        "exact_rational_brute_force": {"shape": f"{tm}x{tn}x{tk}", "seconds": round(exact_s, 3), "cores": 1,
+                                       "flops_per_s": round(2 * tm * tn * tk / exact_s, 1)},
     }
 
 
@@ -283,13 +361,39 @@ def main():
                      "kernel_ms": round(kernel_ms, 5),
                      "algorithmic_bytes": w.algorithmic_bytes()},
     }
+    out["roofline"]["timing"] = (f"HIP events on the launch stream around {args.steps} back-to-back calls, after "
+                                 f"{args.warmup} untimed warm-up calls and {SETTLE_S} s of untimed calls that let the "
+                                 "clocks settle; achieved = algorithmic work / (event time / calls)")
     if spec.kind == "masked":
         gbs = w.algorithmic_bytes() / (kernel_ms * 1e-3) / 1e9
         out["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(gbs / HBM_PEAK_GBS, 4)})
     out["cold"] = cold_entry(w)
+    if out["cold"] is not None:
+        cold_ms = out["cold"]["median_ms"]
+        if spec.kind == "masked":
+            out["roofline"]["frac_cold"] = round(w.algorithmic_bytes() / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        else:
+            out["roofline"]["frac_cold"] = round(flops / (cold_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)
+        out["roofline"]["frac_cold_timing"] = ("median of per-call HIP event times, each call after a 1 GiB read "
+                                               "that evicts the L2 caches and the Infinity Cache")
     if flush is not None:
         out["hbm_copy_gbs"] = round(copy_ceiling_gbs(flush), 1)
+    if not args.no_ceiling:
+        ceil, ceil_promote, ceil32, ceil32_promote = (mfma_ceiling_tflops(v) for v in range(4))
+        out["mfma_ceiling"] = {"tflops": round(ceil, 1), "tflops_with_fp32_promotion": round(ceil_promote, 1),
+                               "tflops_32x32x64": round(ceil32, 1),
+                               "tflops_32x32x64_with_fp32_promotion": round(ceil32_promote, 1),
+                               "what": "FP8 MFMA loop alone (16x16x128, the GEMMs' instruction; 32x32x64 for "
+                                       "comparison), the GEMM's launch shape, random operands"}
+        if spec.kind != "masked":
+            out["roofline"]["frac_of_measured_mfma_ceiling"] = round(achieved / ceil, 4)
+    out["context"] = {
+        "note": "claims for other hardware, quoted as context only (not targets, not baselines)",
+        "ascend_950_dense_gemm": "up to 99.8% of theoretical TFLOPS (BF16/FP8/FP4, shapes not given)",
+        "ascend_950_m_grouped_gemm": "above 800 TFLOPS on realistic expert-token patterns",
+        "source": "third-party summary of the DeepGEMM-Ascend README",
+    }
 
     if args.only is None and not args.no_extra:
         extra = {}

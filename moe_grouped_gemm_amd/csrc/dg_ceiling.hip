@@ -32,15 +32,20 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_ceiling_kernel(const i32x4* 
   f32x4 acc[kChains], tot[kChains];
 #pragma unroll
   for (int c = 0; c < kChains; ++c) acc[c] = tot[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  i32x8 av = a, bv = b;
   for (int it = 0; it < iters; ++it) {
+    // The operands count as new values every iteration (as fragments read
+    // from LDS would be): nothing computed from them can leave the loop.
+    asm volatile("" : "+v"(av), "+v"(bv));
 #pragma unroll
     for (int c = 0; c < kChains; ++c) {
       if constexpr (PROMOTE) {
-        const f32x4 part = mfma_fp8(b, a, (f32x4){0.f, 0.f, 0.f, 0.f});
+        asm volatile("" : "+v"(av));  // a distinct operand per MFMA (no common subexpressions)
+        const f32x4 part = mfma_fp8(bv, av, (f32x4){0.f, 0.f, 0.f, 0.f});
         tot[c] += acc[c] * w;  // the previous MFMA's partial
         acc[c] = part;
       } else {
-        acc[c] = mfma_fp8(b, a, acc[c]);
+        acc[c] = mfma_fp8(bv, av, acc[c]);
       }
     }
   }
@@ -53,7 +58,8 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_ceiling_kernel(const i32x4* 
 // The 32x32x64 shape of the same instruction family for comparison: each
 // MFMA (131072 FLOP) makes a 32x32 float32 block from 32 rows x 64 K of each
 // operand; kChains / 2 accumulators of 16 registers hold as many output
-// values per wave as the 16x16 loop's. PROMOTE: two MFMAs chained per 128-K
+// values per wave as the 16x16 loop's; per iteration they issue two MFMAs
+// each, twice the 16x16 loop's FLOP. PROMOTE: two MFMAs chained per 128-K
 // block, then 16 FMAs of promotion per block (8 per MFMA), one block behind.
 template <bool PROMOTE>
 __global__ void __launch_bounds__(kThreads, 1) mfma32_ceiling_kernel(const i32x4* frag, float* sink, int iters) {
@@ -67,17 +73,20 @@ __global__ void __launch_bounds__(kThreads, 1) mfma32_ceiling_kernel(const i32x4
   f32x16 acc[kC], tot[kC];
 #pragma unroll
   for (int c = 0; c < kC; ++c) acc[c] = tot[c] = (f32x16){};
+  i32x8 av = a, bv = b;
   for (int it = 0; it < iters; ++it) {
+    asm volatile("" : "+v"(av), "+v"(bv));
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
       if constexpr (PROMOTE) {
-        f32x16 part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, (f32x16){}, 0, 0, 0, 0, 0, 0);
-        part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, part, 0, 0, 0, 0, 0, 0);
+        asm volatile("" : "+v"(av));
+        f32x16 part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, (f32x16){}, 0, 0, 0, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, part, 0, 0, 0, 0, 0, 0);
         tot[c] += acc[c] * w;
         acc[c] = part;
       } else {
-        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc[c], 0, 0, 0, 0, 0, 0);
-        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[c], 0, 0, 0, 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[c], 0, 0, 0, 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[c], 0, 0, 0, 0, 0, 0);
       }
     }
   }
@@ -105,8 +114,9 @@ extern "C" dg_status dg_mfma_fp8_ceiling(const void* fragments, float* sink, int
   hipLaunchKernelGGL(kern, dim3(cus), dim3(dg::kThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const dg::i32x4*>(fragments), sink, iters);
   if (hipGetLastError() != hipSuccess) return DG_ERR_LAUNCH;
-  // 16x16: kChains MFMAs of 2*16*16*128 FLOP per iteration; 32x32: kChains / 2
-  // accumulators, two MFMAs of 2*32*32*64 FLOP each -- the same FLOP count.
-  *flops = (long long)cus * (dg::kThreads / 64) * iters * dg::kChains * 2LL * 16 * 16 * 128;
+  // Per wave and iteration, 16x16: kChains MFMAs of 2*16*16*128 FLOP;
+  // 32x32: kChains / 2 accumulators, two MFMAs of 2*32*32*64 FLOP each.
+  const long long per_iter = variant < 2 ? dg::kChains * 2LL * 16 * 16 * 128 : dg::kChains * 2LL * 32 * 32 * 64;
+  *flops = (long long)cus * (dg::kThreads / 64) * iters * per_iter;
   return DG_OK;
 }
