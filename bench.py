@@ -354,7 +354,11 @@ def main():
         "numpy": __import__("numpy").__version__,
         "config": {"workload": spec.name, "kind": spec.kind, "n": spec.n, "k": spec.k,
                    **({"m": spec.m} if spec.kind in ("dense", "k_grouped") else {}),
-                   "accumulate": "fp32 with per-128-K promotion", "output": "bf16", "seed": 0},
+                   "accumulate": ("fp32, E8M0 block scales applied by the MFMA"
+                                  if spec.extra.get("ue8m0") or spec.extra.get("fp4")
+                                  else "fp32 with per-128-K promotion"),
+                   "output": "fp32, accumulated into D in place" if spec.kind == "k_grouped" else "bf16",
+                   "seed": 0},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
                      "kernel": kernel_of(spec),
@@ -380,14 +384,22 @@ def main():
     if flush is not None:
         out["hbm_copy_gbs"] = round(copy_ceiling_gbs(flush), 1)
     if not args.no_ceiling:
-        ceil, ceil_promote, ceil32, ceil32_promote = (mfma_ceiling_tflops(v) for v in range(4))
+        ceil, ceil_promote, ceil32, ceil32_promote, ceil_col = (mfma_ceiling_tflops(v) for v in range(5))
         out["mfma_ceiling"] = {"tflops": round(ceil, 1), "tflops_with_fp32_promotion": round(ceil_promote, 1),
+                               "tflops_with_per_column_promotion": round(ceil_col, 1),
                                "tflops_32x32x64": round(ceil32, 1),
                                "tflops_32x32x64_with_fp32_promotion": round(ceil32_promote, 1),
                                "what": "FP8 MFMA loop alone (16x16x128, the GEMMs' instruction; 32x32x64 for "
-                                       "comparison), the GEMM's launch shape, random operands"}
+                                       "comparison), the GEMM's launch shape, random operands; with the "
+                                       "float32 promotion of the float32-scale GEMMs (per-column: the "
+                                       "K-grouped GEMM's)"}
         if spec.kind != "masked":
+            # Against the loop alone, and against the loop with the same
+            # promotion work as this workload's kernel.
+            e8 = bool(spec.extra.get("ue8m0", False) or spec.extra.get("fp4", False))  # no promotion
+            same = ceil if e8 else (ceil_col if spec.kind == "k_grouped" else ceil_promote)
             out["roofline"]["frac_of_measured_mfma_ceiling"] = round(achieved / ceil, 4)
+            out["roofline"]["frac_of_measured_ceiling_with_same_promotion"] = round(achieved / same, 4)
     out["context"] = {
         "note": "claims for other hardware, quoted as context only (not targets, not baselines)",
         "ascend_950_dense_gemm": "up to 99.8% of theoretical TFLOPS (BF16/FP8/FP4, shapes not given)",

@@ -24,7 +24,12 @@ extern "C" {
  *              GEMMs (four FMAs per MFMA);
  *   variant 2: iters * 16 v_mfma_f32_32x32x64_f8f6f4 (131072 FLOP each, two
  *              per 128-K block), for comparison;
- *   variant 3: variant 2 plus the promotion (16 FMAs per 128-K block).
+ *   variant 3: 32x32x64 with the promotion: per 128-K block two chained
+ *              MFMAs into a partial and 16 FMAs promoting the previous one,
+ *              4 chains per wave (iters * 8 MFMAs);
+ *   variant 4: variant 0 plus the promotion of the K-grouped GEMM, whose
+ *              weights differ per column (four multiplications and four
+ *              FMAs per MFMA).
  *   fragments  device memory, 16-byte aligned, >= 4096 bytes: the operand
  *              bytes every wave multiplies (E4M3 codes; random, non-NaN
  *              values make the clock behave as in a GEMM on random data)

@@ -111,13 +111,30 @@ struct Offsets {
   uint32_t sb_row;  // the RHS scale of the B row this lane holds in the MFMA operand
 };
 
+// The promotion of one band, deferred: the MFMA partial sums of its four
+// 16x16 blocks and their weights sfa[m] * sfb[n].
+struct Pending {
+  f32x4 part[NT];
+  f32x4 w[NT];
+};
+
+__device__ __forceinline__ void clear(Pending& pd) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) pd.part[nt] = pd.w[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+}
+
 // One K block of a wave's 128 x 64 sub-tile from the stage at `st`.
-// Float32 scales: partial sums promoted with each column's own RHS scale.
+// Float32 scales: partial sums promoted with each column's own RHS scale,
+// one band behind: band mt's promotion is issued between band mt + 1's
+// MFMAs, so it never waits for the MFMA it depends on. Band 0 promotes the
+// previous K block's last band, which `pd` carries with its weights (zero
+// at a tile's first block); the block's RHS scales are read only after
+// that, which keeps both sets of registers from being live at once.
 // Power-of-two scales (E8): the MFMA applies them as E8M0 codes, one per
 // lane and operand (the B operand's lane holds row lane % 16 of its 16-row
 // block, the A operand's likewise), and accumulates into the totals.
 template <bool E8>
-__device__ __forceinline__ void block(f32x4 (&acc)[MT][NT], const uint8_t* st, const Offsets& o) {
+__device__ __forceinline__ void block(f32x4 (&acc)[MT][NT], const uint8_t* st, const Offsets& o, Pending& pd) {
   i32x8 bf[NT];
   [[maybe_unused]] f32x4 sb[NT];
   [[maybe_unused]] int eb[NT];
@@ -127,7 +144,6 @@ __device__ __forceinline__ void block(f32x4 (&acc)[MT][NT], const uint8_t* st, c
     const i32x4 y = *reinterpret_cast<const i32x4*>(st + o.b1 + nt * 16 * ROW_BYTES);
     bf[nt] = (i32x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
     if constexpr (E8) eb[nt] = e8m0_code(*reinterpret_cast<const float*>(st + o.sb_row + nt * 64));
-    else sb[nt] = *reinterpret_cast<const f32x4*>(st + o.sb + nt * 64);
   }
   // The A fragment and scale of band mt + 1 are read before band mt's MFMAs
   // are issued, so that the LDS latency hides behind them.
@@ -139,27 +155,67 @@ __device__ __forceinline__ void block(f32x4 (&acc)[MT][NT], const uint8_t* st, c
   };
   i32x8 af[2];
   float sa[2];
+  [[maybe_unused]] f32x4 prev[NT];  // the MFMA partials of band mt - 1
+  [[maybe_unused]] float s_prev = 0.f;
   read_a(0, af[0], sa[0]);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     if (mt + 1 < MT) read_a(mt + 1, af[(mt + 1) & 1], sa[(mt + 1) & 1]);
     const i32x8 a_cur = af[mt & 1];
     const float s_cur = sa[mt & 1];
+    if constexpr (E8) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      if constexpr (E8) {
+      for (int nt = 0; nt < NT; ++nt)
         acc[mt][nt] = mfma_fp8_scaled(bf[nt], a_cur, acc[mt][nt], eb[nt], e8m0_code(s_cur));
-      } else {
-        const f32x4 part = mfma_fp8(bf[nt], a_cur, (f32x4){0.f, 0.f, 0.f, 0.f});
-        acc[mt][nt] += part * (sb[nt] * s_cur);
+    } else {
+      f32x4 part[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        part[nt] = mfma_fp8(bf[nt], a_cur, (f32x4){0.f, 0.f, 0.f, 0.f});
+        if (mt == 0) acc[MT - 1][nt] += pd.part[nt] * pd.w[nt];
+        else acc[mt - 1][nt] += prev[nt] * (sb[nt] * s_prev);
+      }
+      if (mt == 0) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) sb[nt] = *reinterpret_cast<const f32x4*>(st + o.sb + nt * 64);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) prev[nt] = part[nt];
+      s_prev = s_cur;
+      if (mt == MT - 1) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          pd.part[nt] = part[nt];
+          pd.w[nt] = sb[nt] * s_cur;
+        }
       }
     }
     if (mt + 1 < MT) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // the next band's reads first
-    if constexpr (E8) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // the scale code
-    __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);                   // this band's MFMAs
-    if constexpr (!E8) __builtin_amdgcn_sched_group_barrier(0x002, 8 * NT, 0);  // its promotion
+    if constexpr (E8) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // the scale code
+      __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);  // this band's MFMAs
+    } else {
+      // Each MFMA, then a quarter of the previous band's promotion (band 0:
+      // 4 FMAs; later bands 4 multiplications for the weights and 4 FMAs;
+      // the last band also the 16 multiplications of its own weights).
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (mt == 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        else if (mt == MT - 1) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+      if (mt == 0) __builtin_amdgcn_sched_group_barrier(0x100, NT, 0);  // this block's RHS scales
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// The deferred promotion of a tile's last band.
+__device__ __forceinline__ void flush(f32x4 (&acc)[MT][NT], Pending& pd) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[MT - 1][nt] += pd.part[nt] * pd.w[nt];
+  clear(pd);
 }
 
 template <bool HAS_C, bool E8>
@@ -203,6 +259,8 @@ __global__ void __launch_bounds__(THREADS, 1) k_grouped_kernel(KGroupedArgs p) {
     const Tile nx = has_next ? tile_at(p, tn) : tl;
     const bool on = tl.m0 + wm0 < p.m && tl.n0 + wn0 < p.n;
     f32x4 acc[MT][NT];
+    Pending pd;
+    clear(pd);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -228,42 +286,51 @@ __global__ void __launch_bounds__(THREADS, 1) k_grouped_kernel(KGroupedArgs p) {
         issue_block(p, nx, nx.kb0, base + (cs ^ 1) * STAGE_BYTES, wave, lane, lane_off);
         next_loaded = true;
       }
-      if (on) block<E8>(acc, buf + cs * STAGE_BYTES, o);
+      if (on) block<E8>(acc, buf + cs * STAGE_BYTES, o, pd);
     }
+    if constexpr (!E8) flush(acc, pd);
     stage = (stage + tl.nkb) & 1;
     loaded = next_loaded;
 
     if (on) {
-      // Two bands at a time: all their C loads first, then the sums and the
-      // stores. C and D may be one buffer, so the compiler keeps every load
-      // after the stores before it; loading and storing element by element
-      // made each load wait for the one before (32 round trips per tile,
-      // a quarter of the kernel time). Each element is read and written by
-      // this lane only, so reading ahead of the stores is safe.
+      // Buffer loads and stores relative to the tile's first row, clipped
+      // at its last valid row: rows past M read as zero and are not
+      // written, so the code has no per-lane branches. Two bands at a time,
+      // software-pipelined: the C loads of band pair j + 2 are issued right
+      // after the stores of pair j, so that waiting for the loads of pair
+      // j + 1 never waits for stores (a wave's memory operations complete in
+      // issue order). C and D may be one buffer; each element is read and
+      // written by this lane only, so reading ahead of the stores is safe.
+      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+      const size_t tile0 = ((size_t)tl.g * p.m + tl.m0) * (size_t)p.n;
+      const uint32_t tile_bytes = (uint32_t)tl.a_rows * (uint32_t)p.n * 4u;
+      const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(p.d + tile0, tile_bytes);
+      [[maybe_unused]] const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(HAS_C ? p.c + tile0 : p.d + tile0, tile_bytes);
+      const uint32_t lane_off = ((uint32_t)(wm0 + r) * (uint32_t)p.n + (uint32_t)(tl.n0 + wn0 + 4 * q)) * 4u;
+      const uint32_t band_bytes = 16u * (uint32_t)p.n * 4u;
+      f32x4 cv[2][2][NT];
+      auto load_pair = [&](int j, f32x4 (&c2)[2][NT]) {
 #pragma unroll
-      for (int m2 = 0; m2 < MT; m2 += 2) {
-        f32x4 cv[2][NT];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int m = tl.m0 + wm0 + (m2 + h) * 16 + r;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            cv[h][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            if (HAS_C && m < p.m)
-              cv[h][nt] = *reinterpret_cast<const f32x4*>(p.c + ((size_t)tl.g * p.m + m) * p.n + tl.n0 + wn0 +
-                                                          nt * 16 + 4 * q);
-          }
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int m = tl.m0 + wm0 + (m2 + h) * 16 + r;
-          if (m >= p.m) continue;
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
-            const size_t idx = ((size_t)tl.g * p.m + m) * p.n + tl.n0 + wn0 + nt * 16 + 4 * q;
-            *reinterpret_cast<f32x4*>(p.d + idx) = acc[m2 + h][nt] + cv[h][nt];
+            if constexpr (HAS_C)
+              c2[h][nt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        rc, lane_off + nt * 64, (2 * j + h) * band_bytes, 0));
+            else c2[h][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
           }
-        }
+      };
+      load_pair(0, cv[0]);
+      load_pair(1, cv[1]);
+#pragma unroll
+      for (int j = 0; j < MT / 2; ++j) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[2 * j + h][nt] + cv[j & 1][h][nt]),
+                                                   rd, lane_off + nt * 64, (2 * j + h) * band_bytes, 0);
+        if (j + 2 < MT / 2) load_pair(j + 2, cv[j & 1]);
       }
     }
     t = tn;

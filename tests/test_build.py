@@ -42,8 +42,7 @@ def _function_body(asm: str, needle: str) -> str:
 
 def test_zero_scale_codes_select_the_unscaled_mfma(tmp_path):
     asm = _device_asm("dg_ceiling.hip", tmp_path)
-    plain = _function_body(asm, "mfma_ceiling_kernelILb0E")
-    promote = _function_body(asm, "mfma_ceiling_kernelILb1E")
-    for body in (plain, promote):
+    bodies = [_function_body(asm, f"mfma_ceiling_kernelILi{v}E") for v in range(3)]
+    for body in bodies:
         assert re.search(r"\bv_mfma_f32_16x16x128_f8f6f4\b", body)
         assert "v_mfma_scale_f32" not in body
