@@ -413,9 +413,11 @@ def main():
             s = synth.workload_spec(idx)
             wx = synth.make_workload(s, seed=0, device=dev)
             torch.cuda.synchronize()
-            # enough untimed launches for the clocks to settle on each workload
-            steps = max(5, args.steps // 4)
-            ms, kms = time_workload(wx, steps, max(2, args.warmup // 3))
+            # time_workload lets the clocks settle first; at least 50 timed
+            # calls whatever --steps is, so that short runs still average
+            # over many launches
+            steps = max(50, args.steps // 4)
+            ms, kms = time_workload(wx, steps, max(10, args.warmup // 3))
             tf = wx.flops() / (kms * 1e-3) / 1e12
             gbs = wx.algorithmic_bytes() / (kms * 1e-3) / 1e9
             extra[s.name] = {"kernel_ms": round(kms, 5), "tflops": round(tf, 2),
