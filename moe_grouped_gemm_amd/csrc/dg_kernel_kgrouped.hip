@@ -20,9 +20,10 @@
 // after the barrier that frees their stage, then block i is multiplied (one
 // v_mfma_f32_16x16x128_f8f6f4 per 16x16 sub-tile, the B fragment as the
 // first operand, so a lane's four results share one row and cover four
-// consecutive columns) and promoted: total += partial * (sfa[m] * sfb[n]),
-// where the RHS scale now differs per column. The float32 totals, plus C,
-// are stored 16 bytes per lane.
+// consecutive columns) and promoted, one band behind the MFMAs:
+// total += partial * (sfa[m] * sfb[n]), where the RHS scale differs per
+// column. The float32 totals, plus C, leave through 16-byte buffer stores
+// clipped at the tile's last valid row.
 
 #include "dg_device.h"
 
