@@ -791,6 +791,144 @@ def test_k_grouped_many_groups(dev):
 
 
 # ---------------------------------------------------------------------------
+# Seeded random shapes: every layout and scale format on shapes drawn from a
+# fixed generator -- M, row counts and masked counts from 0 or 1 to a few
+# hundred, N a multiple of 128 up to 1152, K from one 128-K block to 40 (both
+# pipelines: the deep one from 32 blocks) -- each compared in full with the
+# oracle. The draw is fixed, so every run checks the same shapes.
+# ---------------------------------------------------------------------------
+
+RANDOM_K_BLOCKS = [1, 2, 3, 5, 8, 16, 31, 32, 40]
+
+
+def _random_cases(kind, count):
+    rng = np.random.default_rng([2027, len(kind)] + [ord(ch) for ch in kind])
+    cases = []
+    for i in range(count):
+        n = 128 * int(rng.integers(1, 10))
+        k = 128 * int(rng.choice(RANDOM_K_BLOCKS))
+        groups = int(rng.integers(1, 7))
+        ue8m0 = i % 3 == 2
+        fp4 = kind.startswith("w4a8")  # W4A8 reads every scale as E8M0: no flag
+        if kind == "dense":
+            cases.append((int(rng.integers(1, 700)), n, k, ue8m0))
+        elif kind in ("contiguous", "w4a8_contiguous"):
+            rows = [int(x) for x in rng.integers(0, 301, groups)]
+            cases.append((rows, n, k) if fp4 else (rows, n, k, ue8m0))
+        elif kind == "nopad":
+            rows = [int(x) for x in rng.integers(0, 301, groups)]
+            cases.append((rows, n, k, int(rng.integers(0, 11)), ue8m0))
+        elif kind in ("masked", "w4a8_masked"):
+            max_m = int(rng.integers(1, 301))
+            counts = [int(x) for x in rng.integers(0, max_m + 1, groups)]
+            cases.append((counts, max_m, n, k) if fp4 else (counts, max_m, n, k, ue8m0))
+        elif kind == "k_grouped":
+            ks = [128 * int(x) for x in rng.integers(0, 13, groups)]
+            cases.append((ks, int(rng.integers(1, 401)), n, ("none", "separate", "in_place")[i % 3], ue8m0))
+    return cases
+
+
+def _e8(w, arr):
+    return O.e8m0_value(arr) if w.ue8m0 else arr
+
+
+@pytest.mark.parametrize("m,n,k,ue8m0", _random_cases("dense", 16))
+def test_random_dense(dev, m, n, k, ue8m0):
+    _say(f"random dense {m}x{n}x{k} ue8m0={ue8m0}")
+    w = synth.make_dense(m, n, k, seed=m * 7 + k, device=dev, ue8m0=ue8m0)
+    d = w.new_output()
+    dg.fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d, ue8m0=ue8m0)
+    torch.cuda.synchronize()
+    ref, mag = _dense_ref(NP(w.a), _e8(w, NP(w.sfa)), NP(w.b), _e8(w, NP(w.sfb)))
+    check_close(NP(d), ref, f"random dense {m}x{n}x{k}", mag, k)
+
+
+@pytest.mark.parametrize("rows,n,k,ue8m0", _random_cases("contiguous", 12))
+def test_random_contiguous(dev, rows, n, k, ue8m0):
+    _say(f"random contiguous rows={rows} n={n} k={k} ue8m0={ue8m0}")
+    w = synth.make_contiguous(rows, n, k, seed=sum(rows) + k, device=dev, poison_padding=True, ue8m0=ue8m0)
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout, ue8m0=ue8m0)
+    torch.cuda.synchronize()
+    _check_contiguous(w, d, f"random contiguous {rows}", _e8(w, NP(w.sfa)), _e8(w, NP(w.sfb)))
+
+
+@pytest.mark.parametrize("counts,max_m,n,k,ue8m0", _random_cases("masked", 12))
+def test_random_masked(dev, counts, max_m, n, k, ue8m0):
+    _say(f"random masked counts={counts} max_m={max_m} n={n} k={k} ue8m0={ue8m0}")
+    w = synth.make_masked(counts, max_m, n, k, seed=max_m + k, device=dev, poison_invalid=True, ue8m0=ue8m0)
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m, ue8m0=ue8m0)
+    torch.cuda.synchronize()
+    _check_masked(w, d, counts, f"random masked {counts}", _e8(w, NP(w.sfa)), _e8(w, NP(w.sfb)))
+
+
+@pytest.mark.parametrize("rows,n,k,tail,ue8m0", _random_cases("nopad", 12))
+def test_random_nopad(dev, rows, n, k, tail, ue8m0):
+    _say(f"random nopad rows={rows} tail={tail} n={n} k={k} ue8m0={ue8m0}")
+    w = synth.make_nopad(rows, n, k, seed=sum(rows) + tail + k, device=dev, tail=tail, poison_tail=True,
+                         ue8m0=ue8m0)
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows, ue8m0=ue8m0)
+    torch.cuda.synchronize()
+    _check_nopad(w, d, f"random nopad {rows}", _e8(w, NP(w.sfa)), _e8(w, NP(w.sfb)))
+
+
+@pytest.mark.parametrize("ks,m,n,c_mode,ue8m0", _random_cases("k_grouped", 12))
+def test_random_k_grouped(dev, ks, m, n, c_mode, ue8m0):
+    _say(f"random k_grouped ks={ks} m={m} n={n} c={c_mode} ue8m0={ue8m0}")
+    if sum(ks) == 0:
+        ks = ks[:-1] + [128]   # K = 0 is rejected; keep the case
+    w = synth.make_k_grouped(ks, m, n, seed=m + sum(ks), device=dev, ue8m0=ue8m0)
+    d = w.new_output()
+    c0 = None if c_mode == "none" else d.clone()
+    if c_mode == "none":
+        d.fill_(float("nan"))
+        dg.k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.ks, ue8m0=ue8m0)
+    elif c_mode == "separate":
+        out = torch.full_like(d, float("nan"))
+        dg.k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, out, w.ks, c=d, ue8m0=ue8m0)
+        torch.cuda.synchronize()
+        assert torch.equal(d, c0), "C was modified"
+        d = out
+    else:
+        dg.k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.ks, c=d, ue8m0=ue8m0)
+    torch.cuda.synchronize()
+    _check_k_grouped(w, d, c0, f"random k_grouped {ks} {c_mode}")
+
+
+@pytest.mark.parametrize("rows,n,k", _random_cases("w4a8_contiguous", 8))
+def test_random_fp8_fp4_contiguous(dev, rows, n, k):
+    _say(f"random w4a8 contiguous rows={rows} n={n} k={k}")
+    w = synth.make_contiguous(rows, n, k, seed=sum(rows) + k + 1, device=dev, poison_padding=True, fp4=True)
+    d = w.new_output()
+    dg.m_grouped_fp8_fp4_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout)
+    torch.cuda.synchronize()
+    got, owner = NP(d), O.contiguous_row_groups(NP(w.layout), w.num_groups)
+    for g in range(w.num_groups):
+        idx = np.nonzero(owner == g)[0]
+        if idx.size:
+            _check_fp4(got[idx], _fp4_ref_rows(w, g, idx, np.arange(w.n)), f"random w4a8 contiguous group {g}", k)
+    check_untouched(got[owner < 0], "random w4a8 contiguous padding rows")
+
+
+@pytest.mark.parametrize("counts,max_m,n,k", _random_cases("w4a8_masked", 8))
+def test_random_fp8_fp4_masked(dev, counts, max_m, n, k):
+    _say(f"random w4a8 masked counts={counts} max_m={max_m} n={n} k={k}")
+    w = synth.make_masked(counts, max_m, n, k, seed=max_m + k + 1, device=dev, poison_invalid=True, fp4=True)
+    d = w.new_output()
+    dg.m_grouped_fp8_fp4_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m)
+    torch.cuda.synchronize()
+    got = NP(d)
+    for g, c in enumerate(counts):
+        v = min(max(int(c), 0), max_m)
+        if v:
+            _check_fp4(got[g, :v], _fp4_ref_rows(w, g, np.arange(v), np.arange(n), NP(w.a)[g], NP(w.sfa)[g]),
+                       f"random w4a8 masked group {g}", k)
+        check_untouched(got[g, v:], f"random w4a8 masked group {g} rows >= {v}")
+
+
+# ---------------------------------------------------------------------------
 # The benchmark workloads at full size: every valid element
 # ---------------------------------------------------------------------------
 #
