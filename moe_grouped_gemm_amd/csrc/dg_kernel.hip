@@ -141,12 +141,11 @@ __device__ __forceinline__ StageSrc stage_src(const TileSrc& t, int kb, int ld_s
   return r;
 }
 
-// The loads of one K block into stage S are issued in STAGE_PARTS parts
-// (see the K loop for when): part 0 and 1 the A tile (rows past the tile's
-// valid rows read as zero), part 2 and 3 the B tile (both with the swizzle of
+// The loads of one K block into stage S are issued in four parts (see the K
+// loop for when): part 0 and 1 the A tile (rows past the tile's valid rows
+// read as zero), part 2 and 3 the B tile (both with the swizzle of
 // lds_offset()), part 3 also the tile's LHS scales and the RHS scale of this
 // wave's columns (returned; usable once the stage has been waited for).
-constexpr int STAGE_PARTS = 4;
 
 template <class C, int S, int PART>
 __device__ __forceinline__ float issue_part(const StageSrc& r, int wave, const LaneOffsets& lo) {

@@ -168,7 +168,7 @@ __device__ __forceinline__ StageSrc stage_src(const TileSrc& t, int kb, int ld_s
 // and 2 of the wave: tile rows [0, 64) and [128, 192)), its LHS scales and
 // the RHS scale of this wave's columns (one float per wave).
 template <class C, int S, int PART>
-__device__ __forceinline__ void issue_x(const StageSrc& r, int wave, int lane, const LaneOffsets& lo) {
+__device__ __forceinline__ void issue_x(const StageSrc& r, int wave, const LaneOffsets& lo) {
   const uint32_t x = region_addr<C, S, 0>();
   if constexpr (PART < 2) {
 #pragma unroll
@@ -186,7 +186,7 @@ __device__ __forceinline__ void issue_x(const StageSrc& r, int wave, int lane, c
 // Group Y of one K block into stage S, in two parts: A half 1 (loads 1 and
 // 3 of the wave: tile rows [64, 128) and [192, 256)), then its LHS scales.
 template <class C, int S, int PART>
-__device__ __forceinline__ void issue_y(const StageSrc& r, int wave, int lane, const LaneOffsets& lo) {
+__device__ __forceinline__ void issue_y(const StageSrc& r, int wave, const LaneOffsets& lo) {
   const uint32_t y = region_addr<C, S, 1>();
   buf_dma16(r.a, lo.ab, (2 * PART + 1) * lo.ab_step, y + (PART * C::NW + wave) * 1024);
   if constexpr (PART == 1) buf_dma4(r.sa, lo.sa, lo.sa_s + 64u * 4u, y + C::Y_SA_OFF + (wave / C::WAVES_N) * 256);
@@ -405,7 +405,7 @@ __device__ __forceinline__ void band_mfmas(WaveTile<C>& wt, f32x4 (&part)[C::NT]
 }
 
 template <class C, int S, bool E8>
-__device__ __forceinline__ void step_on(WaveTile<C>& wt, Operands<C>& o, const StageSrc& r2, int wave, int lane,
+__device__ __forceinline__ void step_on(WaveTile<C>& wt, Operands<C>& o, const StageSrc& r2, int wave,
                                         const LdsOffsets& lds, const LaneOffsets& lo) {
   static_assert(C::MT == 8 && C::NT == 4, "pipeline shape");
   constexpr int SN = 1 - S;
@@ -424,7 +424,7 @@ __device__ __forceinline__ void step_on(WaveTile<C>& wt, Operands<C>& o, const S
       __builtin_amdgcn_sched_barrier(0);
       o.af[(mt + 2) % 4] = frag_a<C, S, mt + 2>(lds);
       o.sav[(mt + 2) % 4] = sa_at<C, S, mt + 2>(lds);
-      issue_x<C, S, 0>(r2, wave, lane, lo);
+      issue_x<C, S, 0>(r2, wave, lo);
       if constexpr (!E8) {
         const float w = o.sav[mt % 4] * sb;
 #pragma unroll
@@ -434,8 +434,8 @@ __device__ __forceinline__ void step_on(WaveTile<C>& wt, Operands<C>& o, const S
     } else {
       o.af[(mt + 2) % 4] = frag_a<C, S, mt + 2>(lds);
       o.sav[(mt + 2) % 4] = sa_at<C, S, mt + 2>(lds);
-      if constexpr (mt == BAND_A + 1) issue_x<C, S, 1>(r2, wave, lane, lo);
-      if constexpr (mt == BAND_A + 2) issue_x<C, S, 2>(r2, wave, lane, lo);
+      if constexpr (mt == BAND_A + 1) issue_x<C, S, 1>(r2, wave, lo);
+      if constexpr (mt == BAND_A + 2) issue_x<C, S, 2>(r2, wave, lo);
       band_mfmas<C, E8, mt>(wt, part, o, eb);
       if constexpr (!E8) {
         const float w = o.sav[mt % 4] * sb;
@@ -473,9 +473,9 @@ __device__ __forceinline__ void step_on(WaveTile<C>& wt, Operands<C>& o, const S
       wait_lgkmcnt_0();
       barrier();
       __builtin_amdgcn_sched_barrier(0);
-      issue_y<C, S, 0>(r2, wave, lane, lo);
+      issue_y<C, S, 0>(r2, wave, lo);
     }
-    if (nt == 1) issue_y<C, S, 1>(r2, wave, lane, lo);
+    if (nt == 1) issue_y<C, S, 1>(r2, wave, lo);
     // The next step's operands (at a tile's last step: the next tile's first).
     o.bf[nt] = frag_b<C, SN>(lds, nt);
     if (nt == 0) o.sb = sb_at<C, SN>(wave);
@@ -498,20 +498,20 @@ __device__ __forceinline__ void step_on(WaveTile<C>& wt, Operands<C>& o, const S
 // A step of a wave with nothing to compute in the current tile: its share of
 // the loads and the barriers, then the next step's operands.
 template <class C, int S>
-__device__ __forceinline__ void step_off(Operands<C>& o, const StageSrc& r2, int wave, int lane,
+__device__ __forceinline__ void step_off(Operands<C>& o, const StageSrc& r2, int wave,
                                          const LdsOffsets& lds, const LaneOffsets& lo) {
   constexpr int IN_FLIGHT = C::X_LOADS + C::Y_LOADS;
   wait_vmcnt<IN_FLIGHT>();
   wait_lgkmcnt_0();
   barrier();
-  issue_x<C, S, 0>(r2, wave, lane, lo);
-  issue_x<C, S, 1>(r2, wave, lane, lo);
-  issue_x<C, S, 2>(r2, wave, lane, lo);
+  issue_x<C, S, 0>(r2, wave, lo);
+  issue_x<C, S, 1>(r2, wave, lo);
+  issue_x<C, S, 2>(r2, wave, lo);
   wait_vmcnt<IN_FLIGHT>();
   wait_lgkmcnt_0();
   barrier();
-  issue_y<C, S, 0>(r2, wave, lane, lo);
-  issue_y<C, S, 1>(r2, wave, lane, lo);
+  issue_y<C, S, 0>(r2, wave, lo);
+  issue_y<C, S, 1>(r2, wave, lo);
   read_first<C, 1 - S>(o, lds, wave);
 }
 
@@ -536,7 +536,7 @@ __device__ __forceinline__ void zero_acc(WaveTile<C>& wt) {
 // leaves the next one starting on the other stage).
 template <class C, int KIND, int PHASE, bool E8>
 __device__ __forceinline__ void tile_loop(const GemmArgs& p, const TileSrc& t0, const TileSrc& t1, const TileSrc& t2,
-                                          WaveTile<C>& wt, int wave, int lane, const LdsOffsets& lds,
+                                          WaveTile<C>& wt, int wave, const LdsOffsets& lds,
                                           const LaneOffsets& lo) {
   const int k_blocks = p.k / BK;
   Operands<C> op;
@@ -549,8 +549,8 @@ __device__ __forceinline__ void tile_loop(const GemmArgs& p, const TileSrc& t0, 
       // The refills are issued unconditionally (past the last tile they load
       // a block nobody reads).
       const StageSrc r2 = refill_src(t0, t1, t2, kb + 2, p, k_blocks);
-      if (wt.on) step_on<C, S, E8>(wt, op, r2, wave, lane, lds, lo);
-      else step_off<C, S>(op, r2, wave, lane, lds, lo);
+      if (wt.on) step_on<C, S, E8>(wt, op, r2, wave, lds, lo);
+      else step_off<C, S>(op, r2, wave, lds, lo);
     });
   }
 }
@@ -609,18 +609,18 @@ __global__ void __launch_bounds__(C::THREADS, 1) fp8_gemm_nt_kernel(GemmArgs p) 
   {
     const StageSrc r0 = refill_src(c0, c1, c2, 0, p, k_blocks);
     const StageSrc r1 = refill_src(c0, c1, c2, 1, p, k_blocks);
-    issue_x<C, 0, 0>(r0, wave, lane, lo);
-    issue_x<C, 0, 1>(r0, wave, lane, lo);
-    issue_x<C, 0, 2>(r0, wave, lane, lo);
-    issue_y<C, 0, 0>(r0, wave, lane, lo);
-    issue_y<C, 0, 1>(r0, wave, lane, lo);
-    issue_x<C, 1, 0>(r1, wave, lane, lo);
-    issue_x<C, 1, 1>(r1, wave, lane, lo);
-    issue_x<C, 1, 2>(r1, wave, lane, lo);
+    issue_x<C, 0, 0>(r0, wave, lo);
+    issue_x<C, 0, 1>(r0, wave, lo);
+    issue_x<C, 0, 2>(r0, wave, lo);
+    issue_y<C, 0, 0>(r0, wave, lo);
+    issue_y<C, 0, 1>(r0, wave, lo);
+    issue_x<C, 1, 0>(r1, wave, lo);
+    issue_x<C, 1, 1>(r1, wave, lo);
+    issue_x<C, 1, 2>(r1, wave, lo);
     wait_vmcnt<C::X_LOADS + C::Y_LOADS>();
     barrier();
-    issue_y<C, 1, 0>(r1, wave, lane, lo);
-    issue_y<C, 1, 1>(r1, wave, lane, lo);
+    issue_y<C, 1, 0>(r1, wave, lo);
+    issue_y<C, 1, 1>(r1, wave, lo);
   }
   int phase = 0;
 
@@ -632,8 +632,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) fp8_gemm_nt_kernel(GemmArgs p) 
     wt.on = tile_on<C, KIND>(p, cur, cmask, wm0, wn0);
     if constexpr (KIND == KIND_CONTIGUOUS) rg = load_row_groups<C>(p, nxt, wm0, lane);
     zero_acc(wt);
-    if (phase == 0) tile_loop<C, KIND, 0, E8>(p, c0, c1, c2, wt, wave, lane, lds, lo);
-    else tile_loop<C, KIND, 1, E8>(p, c0, c1, c2, wt, wave, lane, lds, lo);
+    if (phase == 0) tile_loop<C, KIND, 0, E8>(p, c0, c1, c2, wt, wave, lds, lo);
+    else tile_loop<C, KIND, 1, E8>(p, c0, c1, c2, wt, wave, lds, lo);
     phase = (phase + k_blocks) % 2;
 
     // The next tile's row mask: its row groups were loaded when this tile

@@ -228,7 +228,6 @@ __global__ void __launch_bounds__(Cfg::THREADS, 1) fp8_fp4_gemm_kernel(GemmArgs 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave / Cfg::WAVES_N) * Cfg::WM;
   const int wn0 = (wave % Cfg::WAVES_N) * Cfg::WN;
-  const int r = lane & 15, q = lane >> 4;
   const int k_blocks = p.k / BK;
 
   int num_tiles = p.num_tiles;
