@@ -120,6 +120,12 @@ def set_num_cus(n: int) -> None:
     _check(lib().dg_set_num_cus(int(n)), "dg_set_num_cus")
 
 
+# The names the pages give these helpers ("DeepGEMM for PPU" README,
+# "Utilities"): the persistent grid's width counts compute units here.
+get_num_sms = get_num_cus
+set_num_sms = set_num_cus
+
+
 def get_mn_major_tma_aligned_tensor(sf: torch.Tensor) -> torch.Tensor:
     """Lays out LHS scales [..., M, K/128] (float32) transposed with an aligned
     leading dimension: [..., K/128, tma_aligned(M)], the layout the kernels
