@@ -137,6 +137,11 @@ def get_mn_major_tma_aligned_tensor(sf: torch.Tensor) -> torch.Tensor:
     return out
 
 
+# The older name of the same helper, which the MATE wrapper page still lists
+# among the re-exported utilities.
+get_col_major_tma_aligned_tensor = get_mn_major_tma_aligned_tensor
+
+
 # ---------------------------------------------------------------------------
 # The GEMMs
 # ---------------------------------------------------------------------------
