@@ -791,6 +791,89 @@ def test_k_grouped_many_groups(dev):
 
 
 # ---------------------------------------------------------------------------
+# Small persistent grids: every kernel with 1, 3 and 8 workgroups, so that one
+# workgroup walks many tiles (3 also leaves the XCD renumbering off). The
+# grid changes which tiles share a workgroup, not the arithmetic, so the
+# output must equal the default grid's bit for bit; it is also checked
+# against the oracle. K = 128 gives one K block per tile (the refills then
+# reach the tile after next); K-grouped groups of zero and one K block
+# exercise its first-block hand-over.
+# ---------------------------------------------------------------------------
+
+SMALL_GRID_CASES = [
+    ("dense", dict(m=700, n=640, k=128)),
+    ("dense", dict(m=700, n=640, k=640)),
+    ("dense", dict(m=300, n=896, k=4096)),
+    ("contiguous", dict(rows=[300, 0, 129, 512], n=384, k=256)),
+    ("contiguous", dict(rows=[300, 0, 129, 512], n=384, k=4096)),
+    ("nopad", dict(rows=[300, 0, 129, 77], n=384, k=384)),
+    ("k_grouped", dict(ks=[128, 0, 384, 128, 256], m=300, n=384)),
+    ("w4a8_contiguous", dict(rows=[300, 0, 129], n=384, k=512)),
+]
+
+
+def _small_grid_run(kind, w):
+    if kind == "k_grouped":
+        d = w.new_output()
+        dg.k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.ks)
+    else:
+        d = w.new_output()
+        if kind == "dense":
+            dg.fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d)
+        elif kind == "contiguous":
+            dg.m_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout)
+        elif kind == "nopad":
+            dg.m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows)
+        else:
+            dg.m_grouped_fp8_fp4_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout)
+    torch.cuda.synchronize()
+    return d
+
+
+@pytest.mark.parametrize("cus", [1, 3, 8])
+@pytest.mark.parametrize("kind,args", SMALL_GRID_CASES)
+def test_small_grids(dev, kind, args, cus):
+    _say(f"small grid {kind} {args} cus={cus}")
+    if kind == "dense":
+        w = synth.make_dense(args["m"], args["n"], args["k"], seed=args["k"], device=dev)
+    elif kind == "contiguous":
+        w = synth.make_contiguous(args["rows"], args["n"], args["k"], seed=args["k"], device=dev, poison_padding=True)
+    elif kind == "nopad":
+        w = synth.make_nopad(args["rows"], args["n"], args["k"], seed=args["k"], device=dev, tail=5, poison_tail=True)
+    elif kind == "k_grouped":
+        w = synth.make_k_grouped(args["ks"], args["m"], args["n"], seed=args["m"], device=dev)
+    else:
+        w = synth.make_contiguous(args["rows"], args["n"], args["k"], seed=args["k"], device=dev,
+                                  poison_padding=True, fp4=True)
+    ref = _small_grid_run(kind, w)
+    dg.set_num_cus(cus)
+    try:
+        d = _small_grid_run(kind, w)
+    finally:
+        dg.set_num_cus(0)
+    what = f"small grid {kind} cus={cus}"
+    if kind == "k_grouped":
+        assert torch.equal(d, ref), f"{what}: differs from the default grid"
+        _check_k_grouped(w, d, None, what)
+        return
+    assert torch.equal(d.view(torch.int16), ref.view(torch.int16)), f"{what}: differs from the default grid"
+    if kind == "dense":
+        r, mag = _dense_ref(NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb))
+        check_close(NP(d), r, what, mag, w.k)
+    elif kind == "contiguous":
+        _check_contiguous(w, d, what)
+    elif kind == "nopad":
+        _check_nopad(w, d, what)
+    else:
+        got, owner = NP(d), O.contiguous_row_groups(NP(w.layout), w.num_groups)
+        for g in range(w.num_groups):
+            idx = np.nonzero(owner == g)[0]
+            if idx.size:
+                _check_fp4(got[idx], _fp4_ref_rows(w, g, idx, np.arange(w.n)), f"{what} group {g}", w.k)
+        check_untouched(got[owner < 0], what + " padding rows")
+
+
+# ---------------------------------------------------------------------------
 # Seeded random shapes: every layout and scale format on shapes drawn from a
 # fixed generator -- M, row counts and masked counts from 0 or 1 to a few
 # hundred, N a multiple of 128 up to 1152, K from one 128-K block to 40 (both
