@@ -874,6 +874,68 @@ def test_small_grids(dev, kind, args, cus):
 
 
 # ---------------------------------------------------------------------------
+# Graph capture of every other entry point: one captured call, replayed three
+# times with new operand values copied in between and eager work between the
+# replays; every replay must equal an eager call bit for bit.
+# ---------------------------------------------------------------------------
+
+def _graph_case(kind, dev):
+    """(workload, a function that launches the call writing into d)."""
+    if kind == "dense":
+        w = synth.make_dense(300, 384, 1024, seed=41, device=dev)
+        return w, lambda d: dg.fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d)
+    if kind == "dense_ue8m0":
+        w = synth.make_dense(300, 384, 4096, seed=42, device=dev, ue8m0=True)
+        return w, lambda d: dg.fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d, ue8m0=True)
+    if kind == "contiguous":
+        w = synth.make_contiguous([130, 0, 77, 256, 1], 256, 512, seed=43, device=dev)
+        return w, lambda d: dg.m_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout)
+    if kind == "k_grouped":
+        w = synth.make_k_grouped([128, 0, 384, 256], 300, 384, seed=44, device=dev)
+        c = torch.randn(w.num_groups, w.m, w.n, device=dev)
+        return w, lambda d: dg.k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.ks, c=c)
+    if kind == "w4a8_contiguous":
+        w = synth.make_contiguous([130, 0, 77, 256, 1], 256, 512, seed=45, device=dev, fp4=True)
+        return w, lambda d: dg.m_grouped_fp8_fp4_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout)
+    w = synth.make_masked([40, 100, 7, 64], 128, 256, 512, seed=46, device=dev, fp4=True)
+    return w, lambda d: dg.m_grouped_fp8_fp4_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m)
+
+
+@pytest.mark.parametrize("kind", ["dense", "dense_ue8m0", "contiguous", "k_grouped", "w4a8_contiguous",
+                                  "w4a8_masked"])
+def test_graph_replay_every_entry_point(dev, kind):
+    _say(f"graph replay {kind}")
+    w, call = _graph_case(kind, dev)
+    d = w.new_output()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        call(d)  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(d)
+    gen = torch.Generator(device=dev)
+    for rep in range(3):
+        # new A values (same scales, so the codes stay valid E4M3 values)
+        gen.manual_seed(100 + rep)
+        perm = torch.randperm(w.a.shape[-1], device=dev, generator=gen)
+        a8 = w.a.view(torch.uint8)
+        a8.copy_(a8[..., perm].clone())
+        (d.view(torch.int16) if d.dtype == torch.bfloat16 else d).fill_(-1)
+        graph.replay()
+        torch.cuda.synchronize()
+        d_eager = w.new_output()
+        call(d_eager)
+        torch.cuda.synchronize()
+        if d.dtype == torch.bfloat16:
+            assert torch.equal(d.view(torch.int16), d_eager.view(torch.int16)), f"{kind} replay {rep}"
+        else:
+            assert torch.equal(d, d_eager), f"{kind} replay {rep}"
+
+
+# ---------------------------------------------------------------------------
 # Seeded random shapes: every layout and scale format on shapes drawn from a
 # fixed generator -- M, row counts and masked counts from 0 or 1 to a few
 # hundred, N a multiple of 128 up to 1152, K from one 128-K block to 40 (both
