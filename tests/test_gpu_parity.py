@@ -935,6 +935,44 @@ def test_graph_replay_every_entry_point(dev, kind):
             assert torch.equal(d, d_eager), f"{kind} replay {rep}"
 
 
+def test_concurrent_streams(dev):
+    """Two calls in flight at once on two streams (a dense GEMM and a masked
+    one; their persistent grids compete for the CUs): each result equals the
+    same call made alone, bit for bit. The library keeps no state between
+    calls apart from the CU-count setting."""
+    wd = synth.make_dense(1000, 1024, 2048, seed=51, device=dev)
+    wm = synth.make_masked([200, 17, 256, 0, 99], 256, 1024, 2048, seed=52, device=dev)
+    dd, dm = wd.new_output(), wm.new_output()
+    dg.fp8_gemm_nt(wd.a, wd.sfa, wd.b, wd.sfb, dd)
+    dg.m_grouped_fp8_gemm_nt_masked(wm.a, wm.sfa, wm.b, wm.sfb, dm, wm.masked_m)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(3):
+        d1, d2 = wd.new_output(), wm.new_output()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            dg.fp8_gemm_nt(wd.a, wd.sfa, wd.b, wd.sfb, d1)
+        with torch.cuda.stream(s2):
+            dg.m_grouped_fp8_gemm_nt_masked(wm.a, wm.sfa, wm.b, wm.sfb, d2, wm.masked_m)
+        torch.cuda.synchronize()
+        assert torch.equal(d1.view(torch.int16), dd.view(torch.int16)), f"dense, round {rep}"
+        assert torch.equal(d2.view(torch.int16), dm.view(torch.int16)), f"masked, round {rep}"
+
+
+@pytest.mark.parametrize("m,n,k", [(64, 128, 262144), (130, 256, 65536)])
+def test_dense_long_k(dev, m, n, k):
+    """2048 and 512 K blocks: long K loops of the deep-prefetch pipeline and
+    large row strides, against the oracle with the per-element bound at that
+    many promotions."""
+    _say(f"dense long K {m}x{n}x{k}")
+    w = synth.make_dense(m, n, k, seed=53, device=dev)
+    d = w.new_output()
+    dg.fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d)
+    torch.cuda.synchronize()
+    ref, mag = _dense_ref(NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb))
+    check_close(NP(d), ref, f"dense long K {m}x{n}x{k}", mag, k)
+
+
 # ---------------------------------------------------------------------------
 # Seeded random shapes: every layout and scale format on shapes drawn from a
 # fixed generator -- M, row counts and masked counts from 0 or 1 to a few
