@@ -303,7 +303,8 @@ def main():
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the GEMM has no cross-GPU step; see the sharding notes in DESIGN.md).", file=sys.stderr)
+              "(the GEMM has no cross-GPU step: sharded by expert or by N, each GPU runs its own "
+              "share as an independent single-GPU call).", file=sys.stderr)
         sys.exit(2)
 
     import torch
