@@ -791,6 +791,75 @@ def test_k_grouped_many_groups(dev):
 
 
 # ---------------------------------------------------------------------------
+# The largest group count each grouped call accepts: the on-device group
+# table of the masked (G + 1 entries) and no-padding (2G + 2) layouts filled
+# to its last entry, and the K-grouped kernel's group offsets in its
+# arguments filled to the last one. The last group always has rows (or K),
+# so that the table's last entries are used. The groups hold a few rows
+# each, so the BF16 outputs are checked as one output: the Frobenius and
+# max-abs pair is a statement about a whole output (on 128 elements a single
+# legitimate midpoint flip of a large element can exceed 1e-3), while the
+# per-element bound and the midpoint rule apply to every element anyway.
+# ---------------------------------------------------------------------------
+
+MAX_GROUPS = {"masked": 4096, "w4a8_masked": 4096, "nopad": 2048, "k_grouped": 512}
+
+
+@pytest.mark.parametrize("kind", list(MAX_GROUPS))
+def test_maximum_group_counts(dev, kind):
+    g_max = MAX_GROUPS[kind]
+    rng = np.random.default_rng([71, g_max, len(kind)])
+    _say(f"{kind}: {g_max} groups")
+    if kind == "k_grouped":
+        ks = [int(x) * 128 for x in rng.integers(0, 2, size=g_max)]
+        ks[-1] = 128
+        w = synth.make_k_grouped(ks, 64, 128, seed=7, device=dev)
+        d = w.new_output()
+        c0 = d.clone()
+        dg.k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.ks, c=d)
+        torch.cuda.synchronize()
+        _check_k_grouped(w, d, c0, kind)
+        return
+    if kind == "nopad":
+        rows = [int(x) for x in rng.integers(0, 4, size=g_max)]
+        rows[-1] = 3
+        w = synth.make_nopad(rows, 128, 128, seed=8, device=dev, tail=5, poison_tail=True)
+        d = w.new_output()
+        dg.m_grouped_fp8_gemm_nt_nopad(w.a, w.sfa, w.b, w.sfb, d, w.group_rows)
+        torch.cuda.synchronize()
+        got, a, sfa, b, sfb = NP(d), NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb)
+        owned = np.zeros(w.m, bool)
+        parts = []
+        for g, (first, end) in enumerate(O.nopad_row_ranges(NP(w.group_rows), w.m)):
+            if end > first:
+                ref, mag = O.dense_f64_at(a, sfa, b[g], sfb[g], np.arange(first, end), np.arange(w.n), abs_sum=True)
+                parts.append((got[first:end], ref, mag))
+                owned[first:end] = True
+        d_all, ref_all, mag_all = (np.concatenate(x) for x in zip(*parts))
+        check_close(d_all, ref_all, kind, mag_all, w.k)
+        check_untouched(got[~owned], kind + " rows no group owns")
+        return
+    fp4 = kind == "w4a8_masked"
+    counts = [int(x) for x in rng.integers(0, 17, size=g_max)]
+    counts[-1] = 16
+    w = synth.make_masked(counts, 16, 128, 128, seed=9, device=dev, poison_invalid=True, fp4=fp4)
+    d = w.new_output()
+    call = dg.m_grouped_fp8_fp4_gemm_nt_masked if fp4 else dg.m_grouped_fp8_gemm_nt_masked
+    call(w.a, w.sfa, w.b, w.sfb, d, w.masked_m)
+    torch.cuda.synchronize()
+    got, a, sfa, b, sfb = NP(d), NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb)
+    ref_at = O.fp8_fp4_f64_at if fp4 else O.dense_f64_at
+    parts = []
+    for g, v in enumerate(counts):
+        if v:
+            ref, mag = ref_at(a[g], sfa[g], b[g], sfb[g], np.arange(v), np.arange(w.n), abs_sum=True)
+            parts.append((got[g, :v], ref, mag))
+        check_untouched(got[g, v:], f"{kind} group {g} rows >= {v}")
+    d_all, ref_all, mag_all = (np.concatenate(x) for x in zip(*parts))
+    check_close(d_all, ref_all, kind, mag_all, w.k)
+
+
+# ---------------------------------------------------------------------------
 # Small persistent grids: every kernel with 1, 3 and 8 workgroups, so that one
 # workgroup walks many tiles (3 also leaves the XCD renumbering off). The
 # grid changes which tiles share a workgroup, not the arithmetic, so the
