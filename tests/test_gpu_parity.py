@@ -791,6 +791,89 @@ def test_k_grouped_many_groups(dev):
 
 
 # ---------------------------------------------------------------------------
+# Special values inside the valid rows: the E4M3 NaN codes (0x7F, 0xFF) and a
+# scale whose E8M0 reading is NaN make the elements they reach NaN and no
+# other (IEEE arithmetic in the oracle fixes which); a zero scale, a negated
+# scale (the E8M0 reading ignores the sign) and everything else are compared
+# as usual. The BF16 outputs are compared as bits where they are NaN-free.
+# ---------------------------------------------------------------------------
+
+def _check_with_nans(got_bits, ref, mag, what, k):
+    d = O.bf16_bits_to_f64(got_bits)
+    assert np.array_equal(np.isnan(d), np.isnan(ref)), (
+        f"{what}: NaN pattern differs, first at {np.argwhere(np.isnan(d) != np.isnan(ref))[:3].tolist()}")
+    finite = ~np.isnan(ref)
+    assert finite.any()
+    check_close(got_bits[finite], ref[finite], what, mag[finite], k)
+
+
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_dense_special_values(dev, ue8m0):
+    m, n, k = 300, 384, 512
+    _say(f"dense special values ue8m0={ue8m0}")
+    w = synth.make_dense(m, n, k, seed=41, device=dev, ue8m0=ue8m0)
+    a8, b8 = w.a.view(torch.uint8), w.b.view(torch.uint8)
+    a8[5, 130] = 0x7F                     # NaN codes: rows 5 and 77, column 300
+    a8[77, 0] = 0xFF
+    b8[300, 511] = 0x7F
+    w.sfa[2, 256:300] = 0.0               # a zero scale: K block 2 of rows 256..299
+    w.sfa[0, 3] = -w.sfa[0, 3]            # a negated scale
+    w.sfb[1, 3] = float("nan")            # RHS scale of columns 128..255, K block 3
+    d = w.new_output()
+    dg.fp8_gemm_nt(w.a, w.sfa, w.b, w.sfb, d, ue8m0=ue8m0)
+    torch.cuda.synchronize()
+    sfa, sfb = NP(w.sfa), NP(w.sfb)
+    if ue8m0:
+        sfa, sfb = O.e8m0_value(sfa), O.e8m0_value(sfb)
+    ref, mag = O.dense_f64_at(NP(w.a), sfa, NP(w.b), sfb, np.arange(m), np.arange(n), abs_sum=True)
+    assert np.isnan(ref[5]).all() and np.isnan(ref[:, 300]).all() and np.isnan(ref[:, 128:256]).all()
+    _check_with_nans(NP(d), ref, mag, f"dense special values ue8m0={ue8m0}", k)
+
+
+def test_masked_special_values(dev):
+    counts, max_m, n, k = [40, 0, 200, 17], 200, 256, 512
+    _say("masked special values")
+    w = synth.make_masked(counts, max_m, n, k, seed=43, device=dev, poison_invalid=True)
+    a8 = w.a.view(torch.uint8)
+    a8[0, 39, 300] = 0x7F                 # the last valid row of group 0
+    a8[2, 0, 0] = 0xFF                    # the first row of group 2
+    w.sfa[3, 1, 0:17] = 0.0               # group 3, K block 1: zero scales
+    d = w.new_output()
+    dg.m_grouped_fp8_gemm_nt_masked(w.a, w.sfa, w.b, w.sfb, d, w.masked_m)
+    torch.cuda.synchronize()
+    got, a, sfa, b, sfb = NP(d), NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb)
+    for g, v in enumerate(counts):
+        if v:
+            ref, mag = O.dense_f64_at(a[g], sfa[g], b[g], sfb[g], np.arange(v), np.arange(n), abs_sum=True)
+            if g in (0, 2):
+                _check_with_nans(got[g, :v], ref, mag, f"masked special values group {g}", k)
+            else:
+                check_close(got[g, :v], ref, f"masked special values group {g}", mag, k)
+        check_untouched(got[g, v:], f"masked special values group {g} rows >= {v}")
+
+
+def test_k_grouped_special_values(dev):
+    """A NaN code in group 1's K range reaches group 1's output row only."""
+    ks, m, n = [256, 384, 128], 130, 256
+    _say("k_grouped special values")
+    w = synth.make_k_grouped(ks, m, n, seed=47, device=dev)
+    w.a.view(torch.uint8)[9, 256 + 200] = 0x7F    # row 9, inside group 1's K columns
+    d = w.new_output()
+    c0 = d.clone()
+    dg.k_grouped_fp8_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.ks, c=d)
+    torch.cuda.synchronize()
+    got = d.detach().cpu().numpy().astype(np.float64)
+    c_np = c0.detach().cpu().numpy()
+    a, sfa, b, sfb = NP(w.a), NP(w.sfa), NP(w.b), NP(w.sfb)
+    for g in range(len(ks)):
+        ref, mag = O.k_grouped_f64_at(a, sfa, b, sfb, w.ks, g, np.arange(m), np.arange(n), c_np, abs_sum=True)
+        assert np.array_equal(np.isnan(got[g]), np.isnan(ref)), f"group {g}: NaN pattern differs"
+        assert np.isnan(ref[9]).all() == (g == 1) and np.isnan(ref).sum() == (n if g == 1 else 0)
+    keep = np.r_[0:9, 10:m]
+    _check_k_grouped(w, d, c0, "k_grouped special values", rows=keep)
+
+
+# ---------------------------------------------------------------------------
 # The largest group count each grouped call accepts: the on-device group
 # table of the masked (G + 1 entries) and no-padding (2G + 2) layouts filled
 # to its last entry, and the K-grouped kernel's group offsets in its
