@@ -873,6 +873,32 @@ def test_k_grouped_special_values(dev):
     _check_k_grouped(w, d, c0, "k_grouped special values", rows=keep)
 
 
+def test_fp8_fp4_special_values(dev):
+    """W4A8 (every scale read as E8M0): a NaN code in A, a NaN RHS scale of
+    one column and 32-K block, and a zero LHS scale (read as 2^-127)."""
+    rows, n, k = [130, 0, 77, 256], 256, 512
+    _say("w4a8 special values")
+    w = synth.make_contiguous(rows, n, k, seed=53, device=dev, poison_padding=True, fp4=True)
+    layout = NP(w.layout)
+    w.a.view(torch.uint8)[int(np.nonzero(layout == 2)[0][5]), 257] = 0xFF
+    w.sfb[0, 3, 17] = float("nan")
+    w.sfa[1, int(np.nonzero(layout == 3)[0][0])] = 0.0
+    d = w.new_output()
+    dg.m_grouped_fp8_fp4_gemm_nt_contiguous(w.a, w.sfa, w.b, w.sfb, d, w.layout)
+    torch.cuda.synchronize()
+    got = NP(d)
+    nan_groups = set()
+    for g in range(w.num_groups):
+        idx = np.nonzero(layout == g)[0]
+        if idx.size:
+            ref, mag = _fp4_ref_rows(w, g, idx, np.arange(n))
+            if np.isnan(ref).any():
+                nan_groups.add(g)
+            _check_with_nans(got[idx], ref, mag, f"w4a8 special values group {g}", k)
+    assert nan_groups == {0, 2}
+    check_untouched(got[layout < 0], "w4a8 special values padding rows")
+
+
 # ---------------------------------------------------------------------------
 # The largest group count each grouped call accepts: the on-device group
 # table of the masked (G + 1 entries) and no-padding (2G + 2) layouts filled
